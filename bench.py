@@ -1,0 +1,262 @@
+"""Benchmark of the MoE expert-dispatch hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input already resident
+in HBM:
+  layout (local experts) -> quant + dispatch -> grouped GEMM1
+  -> layout (all experts, the combine's row map) -> combine.
+Every kernel is timed with HIP events recorded on the stream it is launched
+on (torch's current stream, which the binding passes to the library).
+
+Prints ONE JSON line.  `value` is stage1 = layout + quant + GEMM1 in
+microseconds per step (lower is better); the line also carries the dispatch /
+combine HBM GB/s, the GEMM1 fp8 TFLOP/s, a roofline entry per kernel and the
+CPU oracle timed on a bounded sample of the same workload.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--no-cpu-baseline] [--copy-calib]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "stage1 µs (layout+quant+GEMM1), dispatch/combine HBM GB/s, GEMM1 fp8 TFLOP/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="ep8_2048x8_h7168")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calib", action="store_true",
+                   help="also run a plain 1 GiB device copy (counter calibration)")
+    return p.parse_args()
+
+
+def algorithmic(w, R, U, Rc):
+    """Bytes (or flops) each kernel must move at minimum, per launch."""
+    T, k, H, N, L, E = w.T, w.k, w.H, w.N, w.L, w.E
+    width = w.combine_width
+    lay_local = T * k * 4 + (R * 8 + T * k * 4 + T * 4 + U * 4)
+    lay_full = T * k * 4 + (Rc * 8 + T * k * 4 + T * 4 + T * 4)
+    quant = U * 4 + U * H * 2 + U * H + U * (H // 128) * 4
+    gemm_flop = 2 * R * H * N
+    gemm_bytes = U * (H + H // 32) + L * N * H + L * N * H // (128 * 128) * 4 + R * N * 2
+    combine = Rc * width * 2 + T * k * 8 + T * width * 2
+    return dict(layout_local=lay_local, quant=quant, gemm1_flop=gemm_flop, gemm1_bytes=gemm_bytes,
+                layout_full=lay_full, combine=combine)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    import workloads
+    import combine_expert_histogram_amd as moe
+
+    w = workloads.get(args.workload)
+    d_loc = moe.Dims(S=w.S, Ts=w.Ts, k=w.k, E=w.E, e0=w.e0, L=w.L, H=w.H)
+    d_all = moe.Dims(S=w.S, Ts=w.Ts, k=w.k, E=w.E, e0=0, L=w.E, H=w.H)
+    width = w.combine_width
+    log(f"[bench] workload {w.name}: T={w.T} H={w.H} E={w.E} L={w.L} k={w.k} N={w.N}")
+
+    t0 = time.time()
+    ids, wts = workloads.routing(w)
+    x = workloads.activations(w)
+    wq, ws = workloads.weights(w)
+    Y = workloads.expert_outputs(w)
+    log(f"[bench] inputs generated in {time.time() - t0:.1f}s")
+
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    ids_d = dev(ids.reshape(-1))
+    wts_d = dev(wts.reshape(-1))
+    x_d = dev(x.view(np.int16))
+    wq_d = dev(wq)
+    ws_d = dev(ws)
+    Y_d = dev(Y.view(np.int16)).view(torch.bfloat16)
+    del x, wq, Y
+    lay = moe.alloc_layout(d_loc)
+    lay_all = moe.alloc_layout(d_all)
+    q = torch.empty((w.T, w.H), dtype=torch.uint8, device="cuda")
+    qs = torch.empty((w.T, w.H // 128), dtype=torch.float32, device="cuda")
+    y1 = torch.empty((w.T * w.k, w.N), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((w.T, width), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    names = ["layout_local", "quant", "gemm1", "layout_full", "combine"]
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        moe.route_layout(d_loc, ids_d, lay)
+        if ev: ev[1].record(stream)
+        moe.quant_dispatch(d_loc, x_d, lay, q, qs)
+        if ev: ev[2].record(stream)
+        moe.grouped_gemm1(d_loc, w.N, q, qs, lay, wq_d, ws_d, y1)
+        if ev: ev[3].record(stream)
+        moe.route_layout(d_all, ids_d, lay_all)
+        if ev: ev[4].record(stream)
+        moe.combine(d_all, width, Y_d, lay_all["assign_row"], wts_d, out)
+        if ev: ev[5].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    R, U = (int(v) for v in lay["totals"].cpu())
+    Rc = int(lay_all["totals"][0].cpu())
+    log(f"[bench] R={R} U={U} Rc={Rc}; timing {args.steps} steps")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    per = {n: [] for n in names}
+    for e in evs:
+        for j, n in enumerate(names):
+            per[n].append(e[j].elapsed_time(e[j + 1]) * 1e3)        # us
+    med = {n: float(np.median(v)) for n, v in per.items()}
+    mean = {n: float(np.mean(v)) for n, v in per.items()}
+    log("[bench] per-kernel median us: " + ", ".join(f"{n}={med[n]:.1f}" for n in names))
+
+    alg = algorithmic(w, R, U, Rc)
+    stage1 = float(np.median([sum(per[n][i] for n in ("layout_local", "quant", "gemm1"))
+                              for i in range(args.steps)]))
+    hbm_names = ("layout_local", "quant", "layout_full", "combine")
+    hbm_bytes = sum(alg[n] for n in hbm_names)
+    hbm_time = sum(med[n] for n in hbm_names)
+    hbm_gbs = hbm_bytes / (hbm_time * 1e-6) / 1e9
+    gemm_tflops = alg["gemm1_flop"] / (med["gemm1"] * 1e-6) / 1e12
+
+    def hbm_entry(n):
+        a = alg[n] / (med[n] * 1e-6) / 1e9
+        return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None, "us": round(med[n], 2),
+                "algorithmic_bytes": int(alg[n])}
+
+    kernels = {n: hbm_entry(n) for n in hbm_names}
+    kernels["gemm1"] = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": FP8_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
+                        "traffic": None, "us": round(med["gemm1"], 2),
+                        "algorithmic_flop": int(alg["gemm1_flop"]),
+                        "algorithmic_bytes": int(alg["gemm1_bytes"])}
+    dominant = max(names, key=lambda n: med[n])
+    roof = {k: v for k, v in kernels[dominant].items() if k in ("bound", "achieved", "peak", "unit", "frac",
+                                                                "traffic")}
+    roof["kernel"] = dominant
+
+    if args.copy_calib:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    rec = {
+        "metric": METRIC, "value": round(stage1, 2), "unit": "µs", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3",
+        "data": "synthetic",
+        "config": {"workload": w.name, "sources": w.S, "tokens_per_source": w.Ts, "hidden": w.H,
+                   "experts": w.E, "local_experts": w.L, "top_k": w.k, "gemm1_n": w.N,
+                   "combine_width": width, "rows": R, "slots": U, "combine_rows": Rc},
+        "dispatch_combine_hbm_gbs": round(hbm_gbs, 1),
+        "gemm1_fp8_tflops": round(gemm_tflops, 1),
+        "kernels_us_median": {n: round(med[n], 2) for n in names},
+        "kernels_us_mean": {n: round(mean[n], 2) for n in names},
+        "kernels": kernels,
+        "roofline": roof,
+    }
+
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, ids, wts, lay, lay_all, q, qs, y1, out, Y_d, R, U, stage1)
+
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(w, ids, wts, lay, lay_all, q, qs, y1, out, Y_d, R, U, gpu_stage1_us):
+    """The oracle, as it stands, timed on this host on a bounded sample of the
+    same workload and scaled to the full workload's stage1 in microseconds.
+    Sample: the whole layout; the quant of 2048 slots (scaled by U/2048); GEMM1
+    of 8 whole local experts (scaled by L/8).  The same sample is checked
+    against the GPU's outputs."""
+    import torch
+    import workloads
+    from oracle import gemm1 as og, layout as ol, quant as oq
+    from oracle import bf16 as ob
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    cores = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(0)
+
+    t = time.perf_counter()
+    ref = ol.route_layout(ids, w.S, w.Ts, w.k, w.e0, w.L)
+    t_layout = time.perf_counter() - t
+
+    x = workloads.activations(w)
+    ns = min(2048, U)
+    slots = np.sort(rng.choice(U, ns, replace=False))
+    t = time.perf_counter()
+    rq, rs = oq.quant_dispatch(x, ref["slot_tok"], slots=slots)
+    t_quant = (time.perf_counter() - t) * U / ns
+
+    ne = min(8, w.L)
+    experts = list(range(ne))
+    wq, ws = workloads.weights(w, experts=range(ne))
+    offs = ref["expert_offsets"]
+    rows = np.arange(int(offs[0]), int(offs[ne]))
+    need = np.unique(ref["row_slot"][rows])
+    aq, as_ = oq.quant_dispatch(x, ref["slot_tok"], slots=need)
+    pos = np.zeros(U, np.int64)
+    pos[need] = np.arange(need.size)
+    t = time.perf_counter()
+    yref = og.grouped_gemm1(aq, as_, pos[ref["row_slot"]], offs[: ne + 1], wq, ws, rows=rows)
+    t_gemm = (time.perf_counter() - t) * w.L / ne
+
+    # parity of the sample against the GPU outputs (bit-exact layout/quant,
+    # tolerance for GEMM1)
+    ok_layout = all(np.array_equal(lay[k][: len(ref[k])].cpu().numpy(), ref[k])
+                    for k in ("expert_offsets", "row_slot", "slot_tok", "tok_slot"))
+    ok_quant = bool(np.array_equal(q[torch.from_numpy(slots).cuda()].cpu().numpy(), rq))
+    g = y1[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+    r64 = yref.astype(np.float64)
+    rel = float(np.linalg.norm(g - r64) / np.linalg.norm(r64))
+    total_us = (t_layout + t_quant + t_gemm) * 1e6
+    return {"value": round(total_us, 1), "unit": "µs", "cores": int(min(cores, blas_threads)),
+            "host_cores": cores, "blas_threads": int(blas_threads), "kind": "oracle",
+            "sample": f"full layout; quant of {ns} of {U} slots scaled x{U / ns:.2f}; "
+                      f"GEMM1 of {ne} of {w.L} experts ({rows.size} rows) scaled x{w.L / ne:.1f}",
+            "steps_s": {"layout": round(t_layout, 3), "quant_scaled": round(t_quant, 3),
+                        "gemm1_scaled": round(t_gemm, 3)},
+            "gpu_speedup": round(total_us / gpu_stage1_us, 1),
+            "parity_on_sample": {"layout_bit_exact": bool(ok_layout), "quant_bit_exact": ok_quant,
+                                 "gemm1_rel_l2": rel}}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,186 @@
+/*
+ * moe_hotpath.h - C ABI of the MoE expert-dispatch hot path on one MI355X.
+ *
+ * One GPU's share of an expert-parallel MoE layer: the tokens of S source
+ * regions (the stand-in for the S peer ranks whose rows would land here) are
+ * routed top-k over E experts, of which this GPU owns [e0, e0+L).  Four steps:
+ *
+ *   1. moe_route_layout   - stable counting sort of the (token, expert)
+ *                           assignments into an expert-major row layout with
+ *                           a rowmap and a compact landed-token slot list.
+ *   2. moe_quant_dispatch - each landed token's bf16 row is read once and
+ *                           quantised to fp8 e4m3 with 1x128 block scales into
+ *                           its slot.
+ *   3. moe_grouped_gemm1  - per local expert, Y1 = A * W with A's rows read in
+ *                           place through the rowmap.
+ *   4. moe_combine        - top-k weighted sum of expert outputs back to token
+ *                           order.
+ *
+ * Pages this follows (the text of each is the authority on what is computed):
+ *   "poc(cco): MegaMoE stage1 dispatch over SDMA" (mori pull request 1):
+ *     "What", "How it works now", and the commits "each token read and
+ *     quantised once", "recv_layout", "ready-first / quant-lds-store".
+ *   "EPDispatchKernel" (Mojo ep_comm): wait_for_arrivals_and_compute_offsets,
+ *     copy_received_tokens_to_output.
+ *   "TilePipe": dispatch / push combine kernels.
+ *
+ * Conventions for every call:
+ *   - Every array argument is a DEVICE pointer owned by the caller.  The
+ *     library allocates, frees and synchronises nothing and keeps no state
+ *     between calls; work is enqueued on `hip_stream` (a hipStream_t, NULL for
+ *     the default stream) and the call returns without waiting for it.
+ *   - Counts produced on the device (totals, expert_offsets) stay there; the
+ *     later calls read them on the device, so the four calls can be captured
+ *     in one graph with no host read-back.
+ *   - Returned status codes cover argument validation and launch errors only.
+ *     A fault inside a kernel surfaces at the caller's next synchronisation.
+ *   - Calls are re-entrant.  Calls in flight at the same time need distinct
+ *     output and workspace buffers.
+ *   - Notation: T = S*Ts tokens; global token g = s*Ts + t; R = number of
+ *     local assignments (rows); U = number of landed tokens (slots).
+ */
+#ifndef MOE_HOTPATH_H
+#define MOE_HOTPATH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moe_dims {
+    int32_t num_sources;        /* S  >= 1                                      */
+    int32_t tokens_per_source;  /* Ts >= 0                                      */
+    int32_t top_k;              /* k, 1 <= k <= num_experts                     */
+    int32_t num_experts;        /* E  >= 1                                      */
+    int32_t expert_begin;       /* e0 >= 0, first local expert                  */
+    int32_t num_local_experts;  /* L, 1 <= L, e0 + L <= E, L <= 1024            */
+    int32_t hidden;             /* H, multiple of 128 (the quant block)         */
+} moe_dims;
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,   /* null pointer, size out of range, bad dims   */
+    MOE_ERR_WORKSPACE = -2,     /* workspace missing or smaller than required  */
+    MOE_ERR_UNSUPPORTED = -3,   /* valid but outside what the kernels support  */
+    MOE_ERR_HIP = -4            /* a HIP launch returned an error              */
+} moe_status;
+
+/* Human-readable name of a status code (static storage). */
+const char* moe_status_string(moe_status status);
+
+/*
+ * Buffer capacities for the layout's outputs.
+ *   rows_cap  = T*k  (upper bound of R; a token naming one expert twice gets two
+ *               rows, so R can exceed T)
+ *   slots_cap = T    (upper bound of U)
+ * Host-only; no GPU work.
+ */
+moe_status moe_capacity(const moe_dims* dims, int64_t* rows_cap, int64_t* slots_cap);
+
+/* Workspace bytes moe_route_layout needs for these dims (host-only). */
+moe_status moe_route_layout_workspace(const moe_dims* dims, size_t* bytes);
+
+/*
+ * Step 1: layout.  Stable counting sort of the local assignments by local
+ * expert ("MegaMoE stage1 dispatch over SDMA", commit "recv_layout": the
+ * receiver counts the routes per expert and writes the rowmap and srcmap
+ * tables; "EPDispatchKernel", wait_for_arrivals_and_compute_offsets: the
+ * per-local-expert offsets).  Rows of one expert are contiguous and in
+ * ascending (g, j); experts are not padded.
+ *
+ * In:  topk_ids   int32 [T, k] row-major; id - e0 in [0, L) is local, any other
+ *                 value (negative too) is skipped.
+ * Out (all int32):
+ *      expert_counts    [L]       rows per local expert
+ *      expert_offsets   [L+1]     exclusive prefix of expert_counts; [L] = R
+ *      row_slot         [rows_cap] rowmap: row r -> slot of its token (0..U-1)
+ *      row_assign       [rows_cap] row r -> assignment index g*k + j
+ *      assign_row       [T*k]     assignment -> row, -1 if not local
+ *      tok_slot         [T]       token -> slot, -1 if the token has no local
+ *                                 assignment
+ *      slot_tok         [slots_cap] slot u -> token g, ascending in g
+ *      src_slot_offsets [S+1]     first slot of each source region; [S] = U
+ *      totals           [2]       {R, U}
+ * Entries of row_slot / row_assign past R and of slot_tok past U are not
+ * written.  ws: device workspace of at least moe_route_layout_workspace bytes.
+ */
+moe_status moe_route_layout(const moe_dims* dims, const int32_t* topk_ids,
+                            int32_t* expert_counts, int32_t* expert_offsets,
+                            int32_t* row_slot, int32_t* row_assign, int32_t* assign_row,
+                            int32_t* tok_slot, int32_t* slot_tok, int32_t* src_slot_offsets,
+                            int32_t* totals, void* ws, size_t ws_bytes, void* hip_stream);
+
+/*
+ * Step 2: quant + dispatch.  Each landed token's row is read once and
+ * quantised once into its slot ("MegaMoE stage1 dispatch over SDMA", commit
+ * "each token read and quantised once"; "How it works now": the quant writes
+ * each row once, one contiguous 16 B per lane).
+ *
+ * For slot u < U (U read from totals[1] on the device), token g = slot_tok[u],
+ * and block b < H/128:
+ *   a = max |x[g, 128b .. 128b+127]|;  s = a / 448 (IEEE fp32 division);
+ *   q[u, 128b+i] = e4m3(x[g,128b+i] / s) (IEEE division, round to nearest
+ *   even, saturating at 448, sign kept on zero);  q_scale[u, b] = s;
+ *   a == 0 gives s = 0 and zero bytes.
+ * In:  x_bf16  uint16 (bf16 bits) [T, H];  slot_tok, totals from step 1.
+ * Out: q_e4m3  uint8 [slots_cap, H];  q_scale float32 [slots_cap, H/128].
+ * Rows past U are not written.
+ */
+moe_status moe_quant_dispatch(const moe_dims* dims, const uint16_t* x_bf16,
+                              const int32_t* slot_tok, const int32_t* totals,
+                              uint8_t* q_e4m3, float* q_scale, void* hip_stream);
+
+/* Workspace bytes moe_grouped_gemm1 needs (host-only; currently 0). */
+moe_status moe_grouped_gemm1_workspace(const moe_dims* dims, int32_t n, size_t* bytes);
+
+/*
+ * Step 3: grouped GEMM1 over the local experts, A rows read in place through
+ * the rowmap ("MegaMoE stage1 dispatch over SDMA", "What" and commit 1: GEMM1
+ * reads its fp8 A rows and their block scales through a rowmap).
+ *
+ * For local expert le, row r in [expert_offsets[le], expert_offsets[le+1]) and
+ * column c < n:
+ *   y[r, c] = bf16( sum_h  q[row_slot[r], h] * q_scale[row_slot[r], h/128]
+ *                        * w[le, c, h]    * w_scale[le, c/128, h/128] )
+ * accumulated in fp32 (fp8 MFMA per 128-wide K block, then scaled).
+ * In:  q_e4m3, q_scale from step 2; row_slot, expert_offsets, totals from
+ *      step 1 (expert_offsets and totals are read on the device);
+ *      w_e4m3  uint8 [L, n, H]  (each expert's weight stored K-contiguous:
+ *              element (h, c) of the logical [H, n] weight at [le, c, h]);
+ *      w_scale float32 [L, n/128, H/128]  one scale per 128x128 block.
+ * Out: y_bf16 uint16 (bf16 bits) [rows_cap, n]; rows past R are not written.
+ * n must be a positive multiple of 128.  Row ids outside [0, T) read as zero
+ * rows (they cannot come from step 1).
+ */
+moe_status moe_grouped_gemm1(const moe_dims* dims, int32_t n,
+                             const uint8_t* q_e4m3, const float* q_scale,
+                             const int32_t* row_slot, const int32_t* expert_offsets,
+                             const int32_t* totals,
+                             const uint8_t* w_e4m3, const float* w_scale,
+                             uint16_t* y_bf16, void* ws, size_t ws_bytes, void* hip_stream);
+
+/*
+ * Step 4: combine.  Top-k weighted gather-sum back to token order (TilePipe:
+ * push combine to the token owners; "MegaMoE stage1 dispatch over SDMA",
+ * "What": stage2 + combine).
+ *
+ * For token g < T and column c < width:
+ *   acc = 0 (fp32); for j = 0..k-1: r = assign_row[g*k+j];
+ *   if 0 <= r < y_rows: acc += topk_w[g*k+j] * y[r, c];
+ *   out[g, c] = bf16(acc)  (round to nearest even)
+ * In:  y_bf16 uint16 [y_rows, width]; assign_row int32 [T*k] (from step 1 of a
+ *      layout whose rows index y); topk_w float32 [T, k].
+ * Out: out_bf16 uint16 [T, width].
+ * width must be a positive multiple of 8.
+ */
+moe_status moe_combine(const moe_dims* dims, int32_t width, const uint16_t* y_bf16,
+                       int64_t y_rows, const int32_t* assign_row, const float* topk_w,
+                       uint16_t* out_bf16, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_HOTPATH_H */

@@ -52,8 +52,7 @@ def encode(v) -> np.ndarray:
     return code.astype(np.uint8)
 
 
-def decode(c) -> np.ndarray:
-    """e4m3 bytes -> float32 values (0x7F / 0xFF decode to NaN)."""
+def _decode_formula(c) -> np.ndarray:
     c = np.asarray(c, dtype=np.int64)
     s = np.where((c & 0x80) != 0, -1.0, 1.0)
     ef = (c >> 3) & 0xF
@@ -61,3 +60,14 @@ def decode(c) -> np.ndarray:
     val = np.where(ef == 0, mf * 2.0 ** -9, (1.0 + mf / 8.0) * np.exp2(ef - 7.0))
     val = np.where((ef == 15) & (mf == 7), np.nan, val)
     return (s * val).astype(np.float32)
+
+
+_TABLE = _decode_formula(np.arange(256))   # the formula above, evaluated once per code
+
+
+def decode(c) -> np.ndarray:
+    """e4m3 bytes -> float32 values (0x7F / 0xFF decode to NaN)."""
+    c = np.asarray(c)
+    if c.dtype == np.uint8:
+        return _TABLE[c]
+    return _decode_formula(c)
