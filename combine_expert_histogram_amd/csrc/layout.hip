@@ -9,223 +9,259 @@
 // (token, k-slot) order, so the result is unique and the tables are
 // bit-reproducible run to run.
 //
-// Three launches (no grid-wide barrier: a grid barrier needs co-residency, and
-// on gfx950 cross-workgroup release/acquire costs whole-L2 write-back /
-// invalidate, "cut the whole-L2 cache operations" commit of the same PR):
-//   count   - one wavefront per chunk of CT tokens: per-chunk expert histogram
-//             (LDS atomics; order does not matter for counts) and the chunk's
-//             landed-token count.
-//   scan    - one 1024-thread workgroup: exclusive scan of the histogram in
-//             expert-major order -> each chunk's first row per expert, the
-//             expert offsets, and each chunk's first slot.
-//   scatter - one wavefront per chunk again: ranks every local assignment
-//             among the equal-expert assignments before it in the chunk.  A
-//             pass takes 64 consecutive assignments; lanes with the same expert
-//             find each other through a per-expert 64-bit lane mask in LDS
-//             (ds_or), so a pass costs a fixed handful of LDS round trips
-//             whatever the number of distinct experts in it.
+// Two launches, no grid-wide barrier (a grid barrier needs co-residency, and
+// on gfx950 a cross-workgroup release/acquire writes back / invalidates the
+// whole L2, "cut the whole-L2 cache operations" commit of the same PR):
+//   count - one workgroup per chunk of CB tokens: the chunk's per-expert
+//           histogram (LDS atomics; order does not matter for counts) and its
+//           landed-token count, written expert-major to the workspace.
+//   place - one workgroup per chunk again.  It reads the whole histogram
+//           (at most ~32K ints, L2-resident) to get, per expert, the rows of
+//           all earlier chunks and the expert totals, so no separate scan
+//           launch is needed; then each of its four wavefronts ranks the local
+//           assignments of its quarter of the chunk.  A pass takes 64
+//           consecutive assignments; lanes with the same expert find each
+//           other by OR-ing their lane bit into a per-expert 64-bit mask in
+//           LDS (ds_or_b64), so a pass costs a fixed handful of LDS round trips
+//           whatever the number of distinct experts in it.
 #include "common.h"
 
 namespace {
 
 using moe::Dims;
 
-constexpr int kBlock = 256;                       // 4 wavefronts, one chunk each
+constexpr int kBlock = 256;                       // 4 wavefronts
 constexpr int kWaves = kBlock / MOE_WAVE;
-constexpr int kScanThreads = 1024;
-constexpr int kScanPerThread = 8;
-constexpr int64_t kHistTarget = 32768;            // histogram entries the scan aims for
+constexpr int64_t kHistTarget = 32768;            // histogram entries aimed for
 constexpr int kMaxLocalExperts = 1024;
 
 struct Plan {
-    int64_t CT = 16;   // tokens per chunk
+    int64_t CB = 64;   // tokens per chunk (one workgroup)
     int64_t NC = 0;    // chunks
-    // workspace offsets in int32 units
-    int64_t off_hist = 0, off_base = 0, off_landed = 0, off_slot = 0, total_ints = 0;
+    int64_t off_hist = 0, off_landed = 0, total_ints = 0;   // workspace, int32 units
 };
 
 Plan make_plan(const Dims& d) {
     Plan p;
-    p.CT = 16;
-    auto nchunks = [&](int64_t ct) { return (d.T + ct - 1) / ct; };
-    while (nchunks(p.CT) * d.L > kHistTarget && p.CT < 512) p.CT *= 2;
-    p.NC = nchunks(p.CT);
+    const int64_t cap = d.L > 512 ? 512 : 2048;   // keeps the place kernel under 64 KB LDS
+    auto nchunks = [&](int64_t cb) { return (d.T + cb - 1) / cb; };
+    while (nchunks(p.CB) * d.L > kHistTarget && p.CB < cap) p.CB *= 2;
+    p.NC = nchunks(p.CB);
     auto al = [](int64_t v) { return (v + 63) & ~int64_t(63); };   // 256-byte alignment
     p.off_hist = 0;
-    p.off_base = al(p.off_hist + d.L * p.NC);
-    p.off_landed = al(p.off_base + d.L * p.NC);
-    p.off_slot = al(p.off_landed + p.NC);
-    p.total_ints = al(p.off_slot + p.NC);
+    p.off_landed = al(d.L * p.NC);
+    p.total_ints = al(p.off_landed + p.NC);
     return p;
 }
 
-size_t count_lds(const Dims& d, const Plan& p) { return kWaves * (d.L * 4 + p.CT); }
-size_t scatter_lds(const Dims& d, const Plan& p) {
-    return kWaves * (d.L * 8 + d.L * 4 + p.CT * 4 + p.CT);
+size_t count_lds(const Dims& d, const Plan& p) { return d.L * 4 + p.CB + 64; }
+
+// place kernel LDS: mask[4][L] u64 | wcnt[4][L] | A[L] | Tt[L] | offs[L+1] | misc[16] |
+//                   tslot[CB] | flag[CB]
+struct PlaceLds {
+    size_t mask, wcnt, A, Tt, offs, misc, tslot, flag, total;
+};
+__host__ __device__ PlaceLds place_lds(int64_t L, int64_t CB) {
+    PlaceLds o;
+    o.mask = 0;
+    o.wcnt = o.mask + kWaves * L * 8;
+    o.A = o.wcnt + kWaves * L * 4;
+    o.Tt = o.A + L * 4;
+    o.offs = o.Tt + L * 4;
+    o.misc = o.offs + (L + 1) * 4;
+    o.tslot = (o.misc + 16 * 4 + 15) & ~size_t(15);
+    o.flag = o.tslot + CB * 4;
+    o.total = o.flag + CB;
+    return o;
+}
+
+__device__ __forceinline__ void wave_sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
 }
 
 // ------------------------------------------------------------------ count
 __global__ void __launch_bounds__(kBlock)
-layout_count_kernel(const int32_t* __restrict__ ids, int64_t T, int k, int e0, int L,
-                    int CT, int NC, int32_t* __restrict__ hist, int32_t* __restrict__ landed) {
+layout_count_kernel(const int32_t* __restrict__ ids, int64_t T, int k, int e0, int L, int CB,
+                    int NC, int32_t* __restrict__ hist, int32_t* __restrict__ landed) {
     extern __shared__ __align__(16) unsigned char smem[];
-    const int wave = threadIdx.x / MOE_WAVE;
-    const int lane = threadIdx.x % MOE_WAVE;
-    const int c = blockIdx.x * kWaves + wave;
-    int* cnt = reinterpret_cast<int*>(smem) + wave * L;
-    unsigned char* flag = smem + kWaves * L * 4 + wave * CT;
-
-    for (int i = lane; i < L; i += MOE_WAVE) cnt[i] = 0;
-    for (int i = lane; i < CT; i += MOE_WAVE) flag[i] = 0;
+    int* cnt = reinterpret_cast<int*>(smem);
+    int* red = cnt + L;                                   // 16 ints
+    unsigned char* flag = reinterpret_cast<unsigned char*>(red + 16);
+    const int tid = threadIdx.x;
+    const int c = blockIdx.x;
+    for (int i = tid; i < L; i += kBlock) cnt[i] = 0;
+    for (int i = tid; i < CB; i += kBlock) flag[i] = 0;
     __syncthreads();
 
-    const int64_t t0 = (int64_t)c * CT;
-    const int64_t t1 = c < NC ? min(T, t0 + CT) : t0;
-    for (int64_t a = t0 * k + lane; a < t1 * k; a += MOE_WAVE) {
+    const int64_t t0 = (int64_t)c * CB;
+    const int64_t t1 = min(T, t0 + CB);
+    for (int64_t a = t0 * k + tid; a < t1 * k; a += kBlock) {
         const int le = ids[a] - e0;
         if ((unsigned)le < (unsigned)L) {
             atomicAdd(&cnt[le], 1);
-            flag[a / k - t0] = 1;
+            flag[(int)(a / k - t0)] = 1;
         }
     }
     __syncthreads();
-
-    if (c < NC) {
-        int nl = 0;
-        for (int64_t t = t0 + lane; t < t1; t += MOE_WAVE) nl += flag[t - t0];
-        nl = moe::wave_sum(nl);
-        for (int i = lane; i < L; i += MOE_WAVE) hist[(int64_t)i * NC + c] = cnt[i];
-        if (lane == 0) landed[c] = nl;
-    }
+    int nl = 0;
+    for (int i = tid; i < (int)(t1 - t0); i += kBlock) nl += flag[i];
+    nl = moe::wave_sum(nl);
+    if (tid % MOE_WAVE == 0) red[tid / MOE_WAVE] = nl;
+    for (int i = tid; i < L; i += kBlock) hist[(int64_t)i * NC + c] = cnt[i];
+    __syncthreads();
+    if (tid == 0) landed[c] = red[0] + red[1] + red[2] + red[3];
 }
 
-// ------------------------------------------------------------------ scan
-// Block-wide exclusive scan over n ints in tiles of 1024*8; out(idx, prefix)
-// is called for every index.  Returns the total.
-template <class Out>
-__device__ int block_exclusive_scan(const int32_t* __restrict__ in, int64_t n, Out out) {
-    __shared__ int wsum[kScanThreads / MOE_WAVE];
-    const int tid = threadIdx.x;
-    const int wave = tid / MOE_WAVE, lane = tid % MOE_WAVE;
-    int carry = 0;
-    for (int64_t tile = 0; tile < n; tile += (int64_t)kScanThreads * kScanPerThread) {
-        int v[kScanPerThread];
-        int s = 0;
-#pragma unroll
-        for (int i = 0; i < kScanPerThread; ++i) {
-            const int64_t idx = tile + (int64_t)tid * kScanPerThread + i;
-            v[i] = idx < n ? in[idx] : 0;
-            s += v[i];
-        }
-        const int incl = moe::wave_inclusive_scan(s);
-        if (lane == MOE_WAVE - 1) wsum[wave] = incl;
-        __syncthreads();
-        if (wave == 0) {
-            int x = lane < kScanThreads / MOE_WAVE ? wsum[lane] : 0;
-            x = moe::wave_inclusive_scan(x);
-            if (lane < kScanThreads / MOE_WAVE) wsum[lane] = x;
-        }
-        __syncthreads();
-        int ex = carry + incl - s + (wave ? wsum[wave - 1] : 0);
-        const int tile_total = wsum[kScanThreads / MOE_WAVE - 1];
-#pragma unroll
-        for (int i = 0; i < kScanPerThread; ++i) {
-            const int64_t idx = tile + (int64_t)tid * kScanPerThread + i;
-            if (idx < n) out(idx, ex);
-            ex += v[i];
-        }
-        carry += tile_total;
-        __syncthreads();
-    }
-    return carry;
-}
-
-__global__ void __launch_bounds__(kScanThreads)
-layout_scan_kernel(const int32_t* __restrict__ hist, const int32_t* __restrict__ landed,
-                   int L, int NC, int S, int64_t Ts, int32_t* __restrict__ base,
-                   int32_t* __restrict__ slot_base, int32_t* __restrict__ expert_counts,
-                   int32_t* __restrict__ expert_offsets, int32_t* __restrict__ src_slot_offsets,
-                   int32_t* __restrict__ totals) {
-    __shared__ int offs[kMaxLocalExperts + 1];
-    for (int i = threadIdx.x; i <= L; i += kScanThreads) offs[i] = 0;
-    __syncthreads();
-
-    const int64_t nh = (int64_t)L * NC;
-    const int R = block_exclusive_scan(hist, nh, [&](int64_t idx, int ex) {
-        const int le = (int)(idx / NC);
-        const int c = (int)(idx - (int64_t)le * NC);
-        base[(int64_t)c * L + le] = ex;
-        if (c == 0) offs[le] = ex;
-    });
-    const int U = block_exclusive_scan(landed, NC, [&](int64_t idx, int ex) { slot_base[idx] = ex; });
-    __syncthreads();
-    if (NC == 0) {
-        for (int i = threadIdx.x; i < L; i += kScanThreads) offs[i] = 0;
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) offs[L] = R;
-    __syncthreads();
-    for (int i = threadIdx.x; i < L; i += kScanThreads) {
-        expert_offsets[i] = offs[i];
-        expert_counts[i] = offs[i + 1] - offs[i];
-    }
-    if (threadIdx.x == 0) {
-        expert_offsets[L] = R;
-        totals[0] = R;
-        totals[1] = U;
-    }
-    // Sources whose first token is past the end (the last entry, or every
-    // entry when Ts == 0) start at U; the scatter writes the others.
-    for (int s = threadIdx.x; s <= S; s += kScanThreads)
-        if ((int64_t)s * Ts >= (int64_t)S * Ts) src_slot_offsets[s] = U;
-}
-
-// ------------------------------------------------------------------ scatter
+// ------------------------------------------------------------------ place
 __global__ void __launch_bounds__(kBlock)
-layout_scatter_kernel(const int32_t* __restrict__ ids, int64_t T, int k, int e0, int L,
-                      int CT, int NC, int64_t Ts, const int32_t* __restrict__ base,
-                      const int32_t* __restrict__ slot_base, int32_t* __restrict__ row_slot,
-                      int32_t* __restrict__ row_assign, int32_t* __restrict__ assign_row,
-                      int32_t* __restrict__ tok_slot, int32_t* __restrict__ slot_tok,
-                      int32_t* __restrict__ src_slot_offsets) {
+layout_place_kernel(const int32_t* __restrict__ ids, int64_t T, int k, int e0, int L, int CB,
+                    int NC, int S, int64_t Ts, const int32_t* __restrict__ hist,
+                    const int32_t* __restrict__ landed, int32_t* __restrict__ expert_counts,
+                    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ row_slot,
+                    int32_t* __restrict__ row_assign, int32_t* __restrict__ assign_row,
+                    int32_t* __restrict__ tok_slot, int32_t* __restrict__ slot_tok,
+                    int32_t* __restrict__ src_slot_offsets, int32_t* __restrict__ totals) {
     extern __shared__ __align__(16) unsigned char smem[];
-    const int wave = threadIdx.x / MOE_WAVE;
-    const int lane = threadIdx.x % MOE_WAVE;
-    const int c = blockIdx.x * kWaves + wave;
-    uint64_t* mask = reinterpret_cast<uint64_t*>(smem) + wave * L;
-    int* cnt = reinterpret_cast<int*>(smem + kWaves * L * 8) + wave * L;
-    int* tslot = reinterpret_cast<int*>(smem + kWaves * L * 12) + wave * CT;
-    unsigned char* flag = smem + kWaves * (L * 12 + CT * 4) + wave * CT;
+    const PlaceLds lo = place_lds(L, CB);
+    const int tid = threadIdx.x;
+    const int wave = tid / MOE_WAVE;
+    const int lane = tid % MOE_WAVE;
+    const int c = blockIdx.x;                              // may be >= NC when T == 0
+    uint64_t* mask = reinterpret_cast<uint64_t*>(smem + lo.mask) + wave * L;
+    int* wcnt_all = reinterpret_cast<int*>(smem + lo.wcnt);
+    int* wcnt = wcnt_all + wave * L;
+    int* A = reinterpret_cast<int*>(smem + lo.A);          // rows of this expert in chunks < c
+    int* Tt = reinterpret_cast<int*>(smem + lo.Tt);        // expert totals
+    int* offs = reinterpret_cast<int*>(smem + lo.offs);
+    int* misc = reinterpret_cast<int*>(smem + lo.misc);    // [0] slots before c, [1] U, [4..8) wave landed
+    int* tslot = reinterpret_cast<int*>(smem + lo.tslot);
+    unsigned char* flag = smem + lo.flag;
 
-    const int64_t t0 = (int64_t)c * CT;
-    const int64_t t1 = c < NC ? min(T, t0 + CT) : t0;
-    for (int i = lane; i < L; i += MOE_WAVE) {
-        mask[i] = 0;
-        cnt[i] = c < NC ? base[(int64_t)c * L + i] : 0;
+    for (int i = tid; i < L; i += kBlock) {
+        A[i] = 0;
+        Tt[i] = 0;
     }
-    for (int i = lane; i < CT; i += MOE_WAVE) flag[i] = 0;
+    for (int i = tid; i < kWaves * L; i += kBlock) {
+        wcnt_all[i] = 0;
+        reinterpret_cast<uint64_t*>(smem + lo.mask)[i] = 0ull;
+    }
+    for (int i = tid; i < CB; i += kBlock) flag[i] = 0;
+    if (tid < 16) misc[tid] = 0;
     __syncthreads();
 
-    // landed flags
-    for (int64_t a = t0 * k + lane; a < t1 * k; a += MOE_WAVE) {
+    // (1) prefix information from the histogram: each thread sums a
+    // contiguous run of the expert-major histogram, split at chunk c.
+    {
+        const int n = L * NC;
+        const int per = (n + kBlock - 1) / kBlock;
+        int i = tid * per;
+        const int i1 = min(n, i + per);
+        if (i < i1) {
+            int le = i / NC, cc = i - le * NC;
+            int sa = 0, st = 0;
+            for (; i < i1; ++i) {
+                const int v = hist[i];
+                st += v;
+                if (cc < c) sa += v;
+                if (++cc == NC || i + 1 == i1) {
+                    if (sa) atomicAdd(&A[le], sa);
+                    if (st) atomicAdd(&Tt[le], st);
+                    sa = st = 0;
+                    cc = 0;
+                    ++le;
+                }
+            }
+        }
+        int lb = 0, lt = 0;
+        for (int j = tid; j < NC; j += kBlock) {
+            const int v = landed[j];
+            lt += v;
+            if (j < c) lb += v;
+        }
+        lb = moe::wave_sum(lb);
+        lt = moe::wave_sum(lt);
+        if (lane == 0) {
+            if (lb) atomicAdd(&misc[0], lb);
+            if (lt) atomicAdd(&misc[1], lt);
+        }
+    }
+
+    // (2) this chunk: wave `wave` owns tokens [tw0, tw1)
+    const int64_t t0 = (int64_t)c * CB;
+    const int64_t t1 = c < NC ? min(T, t0 + CB) : t0;
+    const int CW = CB / kWaves;
+    const int64_t tw0 = min(t1, t0 + (int64_t)wave * CW);
+    const int64_t tw1 = min(t1, tw0 + CW);
+    for (int64_t a = tw0 * k + lane; a < tw1 * k; a += MOE_WAVE) {
         const int le = ids[a] - e0;
-        if ((unsigned)le < (unsigned)L) flag[a / k - t0] = 1;
+        if ((unsigned)le < (unsigned)L) {
+            atomicAdd(&wcnt[le], 1);
+            flag[(int)(a / k - t0)] = 1;
+        }
     }
     __syncthreads();
 
-    // slots: landed tokens numbered in ascending token order
-    int running = c < NC ? slot_base[c] : 0;
-    for (int64_t tb = t0; tb < t1; tb += MOE_WAVE) {
+    // (3) expert offsets; per-wave first row of each expert; slot bases
+    if (wave == 0) {
+        int carry = 0;
+        for (int b = 0; b < L; b += MOE_WAVE) {
+            const int e = b + lane;
+            const int v = e < L ? Tt[e] : 0;
+            const int incl = moe::wave_inclusive_scan(v);
+            if (e < L) offs[e] = carry + incl - v;
+            carry += __shfl(incl, MOE_WAVE - 1, MOE_WAVE);
+        }
+        if (lane == 0) offs[L] = carry;
+    } else if (wave == 1) {
+        for (int w = 0; w < kWaves; ++w) {
+            const int64_t a0 = min(t1, t0 + (int64_t)w * CW), a1 = min(t1, a0 + CW);
+            int cntw = 0;
+            for (int64_t t = a0 + lane; t < a1; t += MOE_WAVE) cntw += flag[(int)(t - t0)];
+            cntw = moe::wave_sum(cntw);
+            if (lane == 0) misc[4 + w] = cntw;
+        }
+    }
+    __syncthreads();
+    for (int le = tid; le < L; le += kBlock) {
+        int run = offs[le] + A[le];
+        for (int w = 0; w < kWaves; ++w) {
+            const int v = wcnt_all[w * L + le];
+            wcnt_all[w * L + le] = run;
+            run += v;
+        }
+    }
+    const int R = offs[L];
+    const int U = misc[1];
+    if (c == 0) {
+        for (int le = tid; le < L; le += kBlock) {
+            expert_offsets[le] = offs[le];
+            expert_counts[le] = Tt[le];
+        }
+        if (tid == 0) {
+            expert_offsets[L] = R;
+            totals[0] = R;
+            totals[1] = U;
+        }
+        for (int s = tid; s <= S; s += kBlock)
+            if ((int64_t)s * Ts >= T) src_slot_offsets[s] = U;   // sources starting at the end
+    }
+    __syncthreads();
+
+    // (4) slots of this wave's tokens, ascending token order
+    int running = misc[0];
+    for (int w = 0; w < wave; ++w) running += misc[4 + w];
+    for (int64_t tb = tw0; tb < tw1; tb += MOE_WAVE) {
         const int64_t t = tb + lane;
-        const bool in = t < t1;
-        const bool f = in && flag[t - t0];
+        const bool in = t < tw1;
+        const bool f = in && flag[(int)(t - t0)];
         const uint64_t bal = __ballot(f);
         const int slot = running + __popcll(bal & moe::lanemask_lt());
         if (in) {
             if (f) {
                 tok_slot[t] = slot;
                 if (slot < T) slot_tok[slot] = (int32_t)t;     // slots_cap = T
-                tslot[t - t0] = slot;
+                tslot[(int)(t - t0)] = slot;
             } else {
                 tok_slot[t] = -1;
             }
@@ -233,26 +269,24 @@ layout_scatter_kernel(const int32_t* __restrict__ ids, int64_t T, int k, int e0,
         }
         running += __popcll(bal);
     }
-    __syncthreads();
+    wave_sync_lds();
 
-    // rows: stable rank of each local assignment within its expert
-    for (int64_t ab = t0 * k; ab < t1 * k; ab += MOE_WAVE) {
+    // (5) rows: stable rank of each local assignment within its expert
+    for (int64_t ab = tw0 * k; ab < tw1 * k; ab += MOE_WAVE) {
         const int64_t a = ab + lane;
-        const bool valid = a < t1 * k;
+        const bool valid = a < tw1 * k;
         const int le = valid ? ids[a] - e0 : -1;
         const bool loc = valid && (unsigned)le < (unsigned)L;
         if (loc) atomicOr(reinterpret_cast<unsigned long long*>(&mask[le]), 1ull << lane);
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-        __builtin_amdgcn_wave_barrier();
+        wave_sync_lds();
         const uint64_t m = loc ? mask[le] : 0ull;
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-        __builtin_amdgcn_wave_barrier();
+        wave_sync_lds();
         const int rank = __popcll(m & moe::lanemask_lt());
         const int leader = loc ? (__ffsll((unsigned long long)m) - 1) : lane;
         int b = 0;
         if (loc && leader == lane) {
-            b = cnt[le];
-            cnt[le] = b + __popcll(m);
+            b = wcnt[le];
+            wcnt[le] = b + __popcll(m);
             mask[le] = 0ull;
         }
         b = __shfl(b, leader, MOE_WAVE);
@@ -260,14 +294,13 @@ layout_scatter_kernel(const int32_t* __restrict__ ids, int64_t T, int k, int e0,
             const int row = b + rank;
             if ((int64_t)row < T * k) {                        // rows_cap = T*k
                 row_assign[row] = (int32_t)a;
-                row_slot[row] = tslot[a / k - t0];
+                row_slot[row] = tslot[(int)(a / k - t0)];
             }
             assign_row[a] = row;
         } else if (valid) {
             assign_row[a] = -1;
         }
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-        __builtin_amdgcn_wave_barrier();
+        wave_sync_lds();
     }
 }
 
@@ -308,30 +341,23 @@ extern "C" moe_status moe_route_layout(const moe_dims* dims, const int32_t* topk
         return MOE_ERR_INVALID_ARG;
     const Plan p = make_plan(d);
     if (!ws || ws_bytes < (size_t)p.total_ints * 4) return MOE_ERR_WORKSPACE;
+    if (p.NC * d.L >= INT32_MAX) return MOE_ERR_UNSUPPORTED;
     hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
     int32_t* w = reinterpret_cast<int32_t*>(ws);
     int32_t* hist = w + p.off_hist;
-    int32_t* base = w + p.off_base;
     int32_t* landed = w + p.off_landed;
-    int32_t* slot_base = w + p.off_slot;
-    const int grid = (int)((p.NC + kWaves - 1) / kWaves);
 
-    if (grid > 0) {
-        hipLaunchKernelGGL(layout_count_kernel, dim3(grid), dim3(kBlock), count_lds(d, p), stream,
-                           topk_ids, d.T, (int)d.k, (int)d.e0, (int)d.L, (int)p.CT, (int)p.NC,
+    if (p.NC > 0) {
+        hipLaunchKernelGGL(layout_count_kernel, dim3((unsigned)p.NC), dim3(kBlock), count_lds(d, p),
+                           stream, topk_ids, d.T, (int)d.k, (int)d.e0, (int)d.L, (int)p.CB, (int)p.NC,
                            hist, landed);
         if ((st = moe::launch_status()) != MOE_OK) return st;
     }
-    hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, hist, landed,
-                       (int)d.L, (int)p.NC, (int)d.S, d.Ts, base, slot_base, expert_counts,
-                       expert_offsets, src_slot_offsets, totals);
-    if ((st = moe::launch_status()) != MOE_OK) return st;
-    if (grid > 0) {
-        hipLaunchKernelGGL(layout_scatter_kernel, dim3(grid), dim3(kBlock), scatter_lds(d, p), stream,
-                           topk_ids, d.T, (int)d.k, (int)d.e0, (int)d.L, (int)p.CT, (int)p.NC, d.Ts,
-                           base, slot_base, row_slot, row_assign, assign_row, tok_slot, slot_tok,
-                           src_slot_offsets);
-        if ((st = moe::launch_status()) != MOE_OK) return st;
-    }
-    return MOE_OK;
+    // at least one workgroup, so that T == 0 still writes the counts and totals
+    const unsigned grid = (unsigned)std::max<int64_t>(p.NC, 1);
+    hipLaunchKernelGGL(layout_place_kernel, dim3(grid), dim3(kBlock), place_lds(d.L, p.CB).total,
+                       stream, topk_ids, d.T, (int)d.k, (int)d.e0, (int)d.L, (int)p.CB, (int)p.NC,
+                       (int)d.S, d.Ts, hist, landed, expert_counts, expert_offsets, row_slot,
+                       row_assign, assign_row, tok_slot, slot_tok, src_slot_offsets, totals);
+    return moe::launch_status();
 }

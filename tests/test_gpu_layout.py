@@ -43,7 +43,7 @@ EDGES = {
     "ragged_sources": dict(S=3, Ts=17, k=5, E=12, e0=2, L=7),
     "wide_L1024": dict(S=8, Ts=512, k=8, E=1024, e0=0, L=1024),
     "no_local_assignment": dict(S=2, Ts=100, k=2, E=16, e0=8, L=8, lo=0, hi=8),
-    "duplicates_in_row": dict(S=1, Ts=4096, k=6, E=5, e0=1, L=3),
+    "duplicates_in_row": dict(S=1, Ts=4096, k=6, E=6, e0=1, L=3),
     "many_chunks": dict(S=8, Ts=8192, k=2, E=64, e0=0, L=8),
 }
 
