@@ -96,6 +96,7 @@ def main():
     q = torch.empty((w.T, w.H), dtype=torch.uint8, device="cuda")
     qs = torch.empty((w.T, w.H // 128), dtype=torch.float32, device="cuda")
     y1 = torch.empty((w.T * w.k, w.N), dtype=torch.bfloat16, device="cuda")
+    g_ws = moe.alloc_gemm1_workspace(d_loc, w.N)
     out = torch.empty((w.T, width), dtype=torch.bfloat16, device="cuda")
     torch.cuda.synchronize()
 
@@ -108,7 +109,7 @@ def main():
         if ev: ev[1].record(stream)
         moe.quant_dispatch(d_loc, x_d, lay, q, qs)
         if ev: ev[2].record(stream)
-        moe.grouped_gemm1(d_loc, w.N, q, qs, lay, wq_d, ws_d, y1)
+        moe.grouped_gemm1(d_loc, w.N, q, qs, lay, wq_d, ws_d, y1, g_ws)
         if ev: ev[3].record(stream)
         moe.route_layout(d_all, ids_d, lay_all)
         if ev: ev[4].record(stream)

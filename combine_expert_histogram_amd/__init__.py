@@ -6,7 +6,7 @@ in-tree by ``python -m combine_expert_histogram_amd.build``); ``binding`` is
 the ctypes layer that passes torch device tensors and torch's current stream.
 """
 from .binding import (  # noqa: F401
-    Dims, MoeError, alloc_layout, combine, grouped_gemm1, lib, moe_capacity, moe_combine,
+    Dims, MoeError, alloc_gemm1_workspace, alloc_layout, combine, grouped_gemm1, lib, moe_capacity, moe_combine,
     moe_grouped_gemm1, moe_grouped_gemm1_workspace, moe_quant_dispatch, moe_route_layout,
     moe_route_layout_workspace, moe_status_string, quant_dispatch, route_layout,
 )

@@ -172,7 +172,7 @@ def moe_grouped_gemm1(d: Dims, n: int, q_e4m3, q_scale, row_slot, expert_offsets
         _ptr(q_scale, "q_scale", 4 * T * (H // 128), 4), _i32(row_slot, "row_slot", rows_cap),
         _i32(expert_offsets, "expert_offsets", L + 1), _i32(totals, "totals", 2),
         _ptr(w_e4m3, "w_e4m3", L * n * H, 1), _ptr(w_scale, "w_scale", 4 * L * (n // 128) * (H // 128), 4),
-        _ptr(y_bf16, "y_bf16", 2 * rows_cap * n, 2), _ptr(ws, "ws"),
+        _ptr(y_bf16, "y_bf16", 2 * rows_cap * n, 2), _ptr(ws, "ws", moe_grouped_gemm1_workspace(d, n)),
         0 if ws is None else ws.numel() * ws.element_size(), _stream())
     _check("moe_grouped_gemm1", st)
 
@@ -219,10 +219,15 @@ def quant_dispatch(d: Dims, x_bf16, lay: dict, q=None, q_scale=None):
     return q, q_scale
 
 
-def grouped_gemm1(d: Dims, n: int, q, q_scale, lay: dict, w_e4m3, w_scale, y=None):
+def alloc_gemm1_workspace(d: Dims, n: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(moe_grouped_gemm1_workspace(d, n) // 4, 1), dtype=torch.float32, device=device)
+
+
+def grouped_gemm1(d: Dims, n: int, q, q_scale, lay: dict, w_e4m3, w_scale, y=None, ws=None):
     y = torch.empty((max(d.T * d.k, 1), n), dtype=torch.bfloat16, device=q.device) if y is None else y
+    ws = alloc_gemm1_workspace(d, n, q.device) if ws is None else ws
     moe_grouped_gemm1(d, n, q, q_scale, lay["row_slot"], lay["expert_offsets"], lay["totals"],
-                      w_e4m3, w_scale, y)
+                      w_e4m3, w_scale, y, ws)
     return y
 
 

@@ -9,49 +9,135 @@
 // The scales are fp32 (not powers of two), so they cannot ride in the MFMA's
 // e8m0 block scales: each 128-wide K block is one fp8 MFMA with a zero
 // accumulator per 16x16 sub-tile (v_mfma_f32_16x16x128_f8f6f4 covers exactly
-// K = 128), and its fp32 result is folded into the running sum with one FMA
-// by sA[row] * sW (precomputed per row and K block in LDS).
+// K = 128), folded into the fp32 running sum by one FMA with sA[row] * sW.
+// The MFMA computes the transposed sub-tile (weight rows as its A operand), so
+// a lane holds 4 consecutive output columns of one row: one row scale per lane
+// and sub-tile row, and 8 contiguous output bytes per lane in the epilogue.
 //
-// Tiles: 128 rows of one expert x 128 columns; 4 wavefronts in 2 x 2, each
-// 64 x 64 = 4 x 4 MFMA sub-tiles.  A (gathered rows) and B (weight rows,
-// K-contiguous) stage through LDS with an XOR swizzle of the 16 B chunk index
-// by row, so the MFMA operand reads (16 rows x 32 B per quarter-wave) spread
-// over the banks.  The grid is persistent; each workgroup derives the tile
-// table (experts x column tiles x row tiles) from expert_offsets on the
-// device, so no host read-back is needed.
+// Tile: BM rows of one expert x 256 columns, eight wavefronts (two per SIMD)
+// in a WM x WN grid, each owning 64 x (256/WN) = 4 x NJ sub-tiles.  Two
+// shapes are built: 128 x 256 with a 3-stage K ring, and 256 x 256 with a
+// 2-stage ring (fewer operand bytes per MAC; the 160 KB LDS holds two of its
+// 66 KB stages).
+//
+// Operand staging: K blocks stream through the LDS ring, filled by
+// global_load_lds_dwordx4 (memory straight to LDS, no staging registers); a
+// stage is waited for with an explicit vmcnt.  Each lane of a direct-to-LDS
+// load lands at base + 16 * lane; the swizzle of the 16 B chunks inside a
+// 128 B row (chunk c of row r sits in slot c ^ (r & 7) ^ ((r >> 3) & 1)) is made
+// by choosing which global chunk each lane fetches: 16 consecutive rows read
+// at one chunk then hit 16 distinct 16 B bank groups of a 256 B window (and 8
+// distinct ones of a 128 B window).
+//
+// Overlap: the operand loads are bounded by the number of L2 requests a CU can
+// keep in flight, so a wavefront that issued all of a stage's loads at once
+// would stall at the issue until the queue drains, with its MFMAs waiting
+// behind.  The loads of the next stage are therefore spread between the MFMA
+// groups of the current K step.
+//
+// The ring stages are distinct LDS objects and the K loop is unrolled by the
+// stage count, so each step reads one stage and fills another by name: the
+// compiler can then prove that the operand reads do not alias the loads in
+// flight into the other stages and keeps only the explicit waits.
+//
+// Row scales: the rows of a tile are gathered, so their scales would cost one
+// scattered 4 B request per row and K block.  A pre-pass writes the scales
+// into a K-block-major table indexed by expert-major row (the caller's
+// workspace), and a stage reads its row scales as one contiguous piece per
+// wavefront.
+//
+// Scheduling: one persistent workgroup per CU walks the tile table (experts
+// in order; per expert, column tiles outer and row tiles inner, so the row
+// tiles that share a weight slab are adjacent) derived on the device from
+// expert_offsets.  Consecutive tile ids go to workgroups of the same XCD
+// (workgroup b runs on XCD b % 8), so the row tiles sharing a weight slab
+// meet in that XCD's L2.  A wavefront whose 64 rows all lie past the expert's
+// last row skips its MFMAs, so a final partial row tile costs accordingly less.
 #include "common.h"
+
+#include <type_traits>
 
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+using moe::u32x4;
 
-constexpr int BM = 128, BN = 128, BK = 128;
-constexpr int kThreads = 256;
+constexpr int BN = 256, BK = 128;
 constexpr int kMaxL = 1024;
+constexpr int kXcds = 8;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 4); }
+template <int BM_, int WM_, int WN_, int NSTAGE_>
+struct Cfg {
+    static constexpr int BM = BM_, WM = WM_, WN = WN_, NSTAGE = NSTAGE_;
+    static constexpr int kWaves = WM * WN;
+    static constexpr int kThreads = kWaves * MOE_WAVE;
+    static constexpr int RW = BM / WM, CW = BN / WN;              // rows / columns of a wavefront
+    static constexpr int MI = RW / 16, NJ = CW / 16;
+    static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
+    static constexpr int S_ROWS = BM / kWaves;                     // row scales loaded per wavefront
+    static constexpr int S_BYTES = kWaves * 256;                   // one 256 B slot per wavefront
+    static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+    static constexpr int A_LOADS = A_BYTES / (16 * 64 * kWaves);   // per wavefront per stage
+    static constexpr int B_LOADS = B_BYTES / (16 * 64 * kWaves);
+    static constexpr int STAGE_LOADS = A_LOADS + B_LOADS + 1;
+    static_assert(RW == 64 && MI == 4, "a wavefront owns 64 rows");
+    static_assert(CW <= 128 && 128 % CW == 0, "a wavefront's columns share one weight scale");
+    static_assert(S_ROWS >= 4 && S_ROWS <= 64 && S_ROWS % 4 == 0 && BM % kWaves == 0,
+                  "row scales split over wavefronts, 4-row groups kept in one slot");
+    static_assert(A_LOADS % 2 == 0 && B_LOADS % 2 == 0, "load parity follows the load index");
+    static_assert(STAGE_LOADS < 64, "vmcnt holds 6 bits");
+    static_assert(NSTAGE == 2 || NSTAGE == 3, "two or three ring stages");
+    static_assert(NSTAGE * STAGE + 2 * (kMaxL + 1) * 4 + BM * 4 <= 160 * 1024, "LDS budget");
+};
 
-__global__ void __launch_bounds__(kThreads)
-grouped_gemm1_kernel(const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
+#define GPTR(p) ((const void __attribute__((address_space(1)))*)(p))
+#define LPTR(p) ((void __attribute__((address_space(3)))*)(p))
+
+// s_waitcnt immediate waiting until at most n vector-memory ops are outstanding
+// (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14)
+constexpr int wait_vm(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14); }
+
+__device__ __forceinline__ void cbarrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <class C>
+__global__ void __launch_bounds__(C::kThreads, 1)
+grouped_gemm1_kernel(const uint8_t* __restrict__ q, const float* __restrict__ row_scale,
                      const int32_t* __restrict__ row_slot, const int32_t* __restrict__ expert_offsets,
                      const uint8_t* __restrict__ w, const float* __restrict__ w_scale,
-                     uint16_t* __restrict__ y, int L, int N, int H, int64_t T, int64_t rows_cap) {
-    __shared__ __align__(16) uint8_t As[BM * BK];
-    __shared__ __align__(16) uint8_t Bs[BN * BK];
-    __shared__ __align__(16) float fs[BM];
-    __shared__ int slot_s[BM];
+                     uint16_t* __restrict__ y, int L, int N, int H, int64_t T, int64_t rows_cap,
+                     int64_t scale_ld) {
+    constexpr int BM = C::BM, kThreads = C::kThreads, MI = C::MI, NJ = C::NJ;
+    constexpr int A_BYTES = C::A_BYTES, B_BYTES = C::B_BYTES, STAGE = C::STAGE;
+    constexpr int A_LOADS = C::A_LOADS, B_LOADS = C::B_LOADS, NLOADS = C::STAGE_LOADS;
+    constexpr int RW = C::RW, CW = C::CW, WN = C::WN;
+    // With S stages, the loads of K block kb+S-1 are issued during step kb; at
+    // the top of step kb the ops outstanding are, in issue order, those of the
+    // stages kb .. kb+S-2, so "at most (S-2) stages outstanding" means stage kb
+    // has landed (loads complete in order).
+    constexpr int kWaitSteady = wait_vm((C::NSTAGE - 2) * NLOADS);
+    constexpr int kWaitAll = wait_vm(0);
+
+    __shared__ __align__(16) uint8_t stage0[STAGE];
+    __shared__ __align__(16) uint8_t stage1[STAGE];
+    __shared__ __align__(16) uint8_t stage2[C::NSTAGE == 3 ? STAGE : 16];
     __shared__ int tstart[kMaxL + 1];     // first tile of each expert
     __shared__ int eoff[kMaxL + 1];
+    __shared__ int slot_s[BM];
 
     const int tid = threadIdx.x;
     const int lane = tid % MOE_WAVE;
-    const int wave = tid / MOE_WAVE;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int NT = N / BN;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / MOE_WAVE);
+    const int wm = wave / WN, wn = wave % WN;
+    const int NT = (N + BN - 1) / BN;                // the last column tile may hold 128
     const int KB = H / BK;
+    const int NB = N / 128;
 
-    // tile table: experts in order, each expert's tiles column-tile-major
+    // tile table
     for (int i = tid; i <= L; i += kThreads) {
         int64_t o = expert_offsets[i];
         eoff[i] = (int)(o < 0 ? 0 : (o > rows_cap ? rows_cap : o));
@@ -74,9 +160,18 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const float* __restrict__ q_
     }
     __syncthreads();
     const int total = tstart[L];
+    const int G = gridDim.x;
+    const int b = blockIdx.x;
+    const int my = (b % kXcds) * (G / kXcds) + b / kXcds;   // G is a multiple of 8
 
-    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-        // expert of this tile: last e with tstart[e] <= tile
+    // Direct-to-LDS load gi (of the workgroup) fills LDS chunks gi*64 + l = row
+    // gi*8 + l/8, slot l%8, which holds global chunk (l%8) ^ (l/8) ^ (gi & 1).
+    const int lrow = lane >> 3;
+    const int gchunk = (lane & 7) ^ lrow;
+
+    for (int it = 0;; ++it) {
+        const int tile = it * G + my;
+        if (tile >= total) break;
         int lo = 0, hi = L - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -91,92 +186,220 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const float* __restrict__ q_
         const int r0 = eoff[e] + mtile * BM;
         const int nvalid = min(BM, eoff[e + 1] - r0);
         const int n0 = nt * BN;
+        const int ncols = min(BN, N - n0);            // 256, or 128 for a final half tile
+        const bool active = wm * RW < nvalid && wn * CW < ncols;   // wavefront has output
 
-        for (int i = tid; i < BM; i += kThreads) {
-            int s = -1;
-            if (i < nvalid) {
-                s = row_slot[r0 + i];
-                if ((uint64_t)s >= (uint64_t)T) s = -1;
+        if (tid < BM) {
+            int s0 = row_slot[r0];
+            if ((uint64_t)s0 >= (uint64_t)T) s0 = 0;
+            int s = s0;                       // rows past the expert reuse row 0's slot
+            if (tid < nvalid) {
+                s = row_slot[r0 + tid];
+                if ((uint64_t)s >= (uint64_t)T) s = s0;
             }
-            slot_s[i] = s;
+            slot_s[tid] = s;
         }
         __syncthreads();
 
-        v4f acc[4][4];
+        uint32_t a_off[A_LOADS];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
+        for (int i = 0; i < A_LOADS; ++i) {
+            const int r = (wave * A_LOADS + i) * 8 + lrow;
+            a_off[i] = (uint32_t)slot_s[r] * (uint32_t)H + (gchunk ^ (i & 1)) * 16;
+        }
         const uint8_t* wexp = w + ((int64_t)e * N + n0) * H;
-        const float* wsc = w_scale + ((int64_t)e * (N / 128) + n0 / 128) * KB;
+        const uint32_t b_lane0 = (uint32_t)lrow * (uint32_t)H + gchunk * 16;
+        const uint32_t b_lane1 = (uint32_t)lrow * (uint32_t)H + (gchunk ^ 1) * 16;
+        const float* wsc = w_scale + ((int64_t)e * NB + min((n0 + wn * CW) / 128, NB - 1)) * KB;
+        const float* srow = row_scale + r0 + wave * C::S_ROWS + min(lane, C::S_ROWS - 1);
 
-        for (int kb = 0; kb < KB; ++kb) {
-            // stage A rows (gathered through the rowmap) and B rows
+        // the idx-th load of stage `kb` into LDS `base` (idx is a compile-time
+        // constant after unrolling)
+        auto issue_one = [&](int idx, int kb, uint8_t* base) {
+            if (idx < A_LOADS) {
+                const int i = idx;
+                __builtin_amdgcn_global_load_lds(GPTR(q + a_off[i] + kb * BK),
+                                                 LPTR(base + (wave * A_LOADS + i) * 1024), 16, 0, 0);
+            } else if (idx < A_LOADS + B_LOADS) {
+                const int i = idx - A_LOADS;
+                // rows past a half tile re-read the first half (their columns are not stored)
+                int rb = (wave * B_LOADS + i) * 8;
+                if (rb >= ncols) rb -= ncols;
+                __builtin_amdgcn_global_load_lds(
+                    GPTR(wexp + (uint32_t)rb * (uint32_t)H + ((i & 1) ? b_lane1 : b_lane0) + kb * BK),
+                    LPTR(base + A_BYTES + (wave * B_LOADS + i) * 1024), 16, 0, 0);
+            } else {
+                // row scales of K block kb: wavefront w loads rows [r0 + w*S_ROWS, +S_ROWS)
+                // into the first S_ROWS floats of its 256 B slot; its other lanes repeat
+                // the last row (same line, no extra request)
+                __builtin_amdgcn_global_load_lds(GPTR(srow + kb * scale_ld),
+                                                 LPTR(base + A_BYTES + B_BYTES + wave * 256), 4, 0, 0);
+            }
+        };
+        auto issue_all = [&](int kb, uint8_t* base) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = (tid >> 3) + 32 * i;
-                const int ch = tid & 7;
-                const int s = slot_s[row];
-                moe::u32x4 va = moe::u32x4{0u, 0u, 0u, 0u};
-                if (s >= 0)
-                    va = *reinterpret_cast<const moe::u32x4*>(q + (int64_t)s * H + kb * BK + ch * 16);
-                *reinterpret_cast<moe::u32x4*>(As + swz(row, ch)) = va;
-                const moe::u32x4 vb =
-                    *reinterpret_cast<const moe::u32x4*>(wexp + (int64_t)row * H + kb * BK + ch * 16);
-                *reinterpret_cast<moe::u32x4*>(Bs + swz(row, ch)) = vb;
-            }
-            if (tid < BM) {
-                const int s = slot_s[tid];
-                fs[tid] = s >= 0 ? q_scale[(int64_t)s * KB + kb] * wsc[kb] : 0.0f;
-            }
-            __syncthreads();
+            for (int d = 0; d < NLOADS; ++d) issue_one(d, kb, base);
+        };
 
-            v8i bf[4];
+        v4f acc[MI][NJ];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int col = wn * 64 + j * 16 + (lane & 15);
-                const int c0 = (lane >> 4) * 2;
-                const moe::u32x4 b0 = *reinterpret_cast<const moe::u32x4*>(Bs + swz(col, c0));
-                const moe::u32x4 b1 = *reinterpret_cast<const moe::u32x4*>(Bs + swz(col, c0 + 1));
-                bf[j] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
-                            (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-            }
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = wm * 64 + i * 16 + (lane & 15);
-                const int c0 = (lane >> 4) * 2;
-                const moe::u32x4 a0 = *reinterpret_cast<const moe::u32x4*>(As + swz(row, c0));
-                const moe::u32x4 a1 = *reinterpret_cast<const moe::u32x4*>(As + swz(row, c0 + 1));
-                const v8i af = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                                   (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-                const v4f f = *reinterpret_cast<const v4f*>(fs + wm * 64 + i * 16 + 4 * (lane >> 4));
+            for (int j = 0; j < NJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+        // One K step: compute from `cur`; when `fill` is set, the loads of K block
+        // kb_fill into `nxt` are spread between the MFMA groups (load d after
+        // column group j = d * NJ / NLOADS).
+        auto step = [&](int kb, const uint8_t* cur, bool fill, int kb_fill, uint8_t* nxt) {
+            const float sw = wsc[kb];
+            const uint8_t* As = cur;
+            const uint8_t* Bs = As + A_BYTES;
+            const float* Ss = reinterpret_cast<const float*>(Bs + B_BYTES);   // per-wavefront scale slots
+            v8i af[MI];
+            float f[MI];
+            if (active) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        af, bf[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) acc[i][j][v] = fmaf(p[v], f[v], acc[i][j][v]);
+                for (int i = 0; i < MI; ++i) {
+                    const int row = wm * RW + i * 16 + (lane & 15);
+                    const int c0 = (lane >> 4) * 2;
+                    const int sw_r = (row & 7) ^ ((row >> 3) & 1);
+                    const u32x4 a0 = *reinterpret_cast<const u32x4*>(As + row * BK + ((c0 ^ sw_r) << 4));
+                    const u32x4 a1 = *reinterpret_cast<const u32x4*>(As + row * BK + (((c0 + 1) ^ sw_r) << 4));
+                    af[i] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+                    f[i] = Ss[(row / C::S_ROWS) * 64 + row % C::S_ROWS] * sw;
                 }
             }
-            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                if (active) {
+                    const int col = wn * CW + j * 16 + (lane & 15);
+                    const int c0 = (lane >> 4) * 2;
+                    const int sw_c = (col & 7) ^ ((col >> 3) & 1);
+                    const u32x4 b0 = *reinterpret_cast<const u32x4*>(Bs + col * BK + ((c0 ^ sw_c) << 4));
+                    const u32x4 b1 = *reinterpret_cast<const u32x4*>(Bs + col * BK + (((c0 + 1) ^ sw_c) << 4));
+                    const v8i bf = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+#pragma unroll
+                    for (int i = 0; i < MI; ++i) {
+                        // transposed sub-tile: lane l holds row (l & 15), columns 4*(l >> 4) + v
+                        const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            bf, af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) acc[i][j][v] = fmaf(p[v], f[i], acc[i][j][v]);
+                    }
+                }
+                if (fill) {
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int d = 0; d < NLOADS; ++d)
+                        if (d * NJ / NLOADS == j) issue_one(d, kb_fill, nxt);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        };
+
+        if constexpr (C::NSTAGE == 3) {
+            // stage 1 is always filled (with K block 0 again when there is one K
+            // block) so that the steady loop starts from the same memory-op count
+            // on every path
+            issue_all(0, stage0);
+            issue_all(KB > 1 ? 1 : 0, stage1);
+            int kb = 0;
+            // steady state: every step refills the stage two ahead, unconditionally,
+            // so the compiler sees the same memory ops on every path
+            for (; kb + 4 < KB; kb += 3) {
+                __builtin_amdgcn_s_waitcnt(kWaitSteady); cbarrier(); step(kb, stage0, true, kb + 2, stage2);
+                __builtin_amdgcn_s_waitcnt(kWaitSteady); cbarrier(); step(kb + 1, stage1, true, kb + 3, stage0);
+                __builtin_amdgcn_s_waitcnt(kWaitSteady); cbarrier(); step(kb + 2, stage2, true, kb + 4, stage1);
+            }
+            // tail (at most 4 K blocks; kb is a multiple of 3 here)
+            auto tail = [&](int k, const uint8_t* cur, uint8_t* nxt2) {
+                if (k >= KB) return;
+                if (k + 1 < KB) __builtin_amdgcn_s_waitcnt(kWaitSteady);
+                else __builtin_amdgcn_s_waitcnt(kWaitAll);
+                cbarrier();
+                step(k, cur, k + 2 < KB, k + 2, nxt2);
+            };
+            tail(kb, stage0, stage2);
+            tail(kb + 1, stage1, stage0);
+            tail(kb + 2, stage2, stage1);
+            tail(kb + 3, stage0, stage2);
+        } else {
+            issue_all(0, stage0);
+            int kb = 0;
+            for (; kb + 2 < KB; kb += 2) {
+                __builtin_amdgcn_s_waitcnt(kWaitAll); cbarrier(); step(kb, stage0, true, kb + 1, stage1);
+                __builtin_amdgcn_s_waitcnt(kWaitAll); cbarrier(); step(kb + 1, stage1, true, kb + 2, stage0);
+            }
+            // tail (one or two K blocks; kb is even here)
+            __builtin_amdgcn_s_waitcnt(kWaitAll);
+            cbarrier();
+            step(kb, stage0, kb + 1 < KB, kb + 1, stage1);
+            if (kb + 1 < KB) {
+                __builtin_amdgcn_s_waitcnt(kWaitAll);
+                cbarrier();
+                step(kb + 1, stage1, false, 0, stage0);
+            }
         }
 
-        // epilogue: bf16 (RNE), valid rows only
+        __builtin_amdgcn_s_waitcnt(kWaitAll);
+        // epilogue: bf16 (RNE), valid rows and columns only; 4 consecutive columns
+        // (8 bytes) per lane and sub-tile
+        if (active) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int row = wm * 64 + i * 16 + 4 * (lane >> 4) + v;
+            for (int i = 0; i < MI; ++i) {
+                const int row = wm * RW + i * 16 + (lane & 15);
                 if (row < nvalid) {
-                    uint16_t* yrow = y + (int64_t)(r0 + row) * N + n0 + wn * 64 + (lane & 15);
+                    uint16_t* yrow = y + (int64_t)(r0 + row) * N + n0 + wn * CW + 4 * (lane >> 4);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) yrow[j * 16] = (uint16_t)moe::f32_to_bf16_rne(acc[i][j][v]);
+                    for (int j = 0; j < NJ; ++j) {
+                        const uint32_t lo = moe::f32_to_bf16_rne(acc[i][j][0]) | (moe::f32_to_bf16_rne(acc[i][j][1]) << 16);
+                        const uint32_t hi = moe::f32_to_bf16_rne(acc[i][j][2]) | (moe::f32_to_bf16_rne(acc[i][j][3]) << 16);
+                        *reinterpret_cast<uint2*>(yrow + j * 16) = make_uint2(lo, hi);
+                    }
                 }
             }
+        }
         __syncthreads();
     }
 }
+
+// Row-scale table: out[kb * scale_ld + r] = q_scale[row_slot[r], kb] for the
+// R expert-major rows (R = expert_offsets[L]).  One thread per row reads its
+// slot's contiguous scales; for a fixed kb, consecutive threads write
+// consecutive floats.  A row id outside [0, T) gets scale 0 (a zero row).
+__global__ void __launch_bounds__(256)
+gather_row_scales_kernel(const float* __restrict__ q_scale, const int32_t* __restrict__ row_slot,
+                         const int32_t* __restrict__ expert_offsets, int L, int KB, int64_t T,
+                         int64_t rows_cap, int64_t scale_ld, float* __restrict__ out) {
+    int64_t R = expert_offsets[L];
+    R = R < 0 ? 0 : (R > rows_cap ? rows_cap : R);
+    for (int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x; r < R; r += (int64_t)gridDim.x * 256) {
+        const int s = row_slot[r];
+        const bool ok = (uint64_t)s < (uint64_t)T;
+        const float* src = q_scale + (int64_t)(ok ? s : 0) * KB;
+        for (int kb = 0; kb < KB; ++kb) out[kb * scale_ld + r] = ok ? src[kb] : 0.0f;
+    }
+}
+
+// Rows of the table: every row a tile can name (rows_cap plus one tile of the
+// largest row count), rounded up to 64 floats.
+constexpr int kMaxBM = 256;
+int64_t scale_ld_of(int64_t rows_cap) { return ((rows_cap + kMaxBM) + 63) & ~int64_t(63); }
+
+int cu_count() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return n;
+}
+
+#ifndef MOE_GEMM1_TILE_M
+#define MOE_GEMM1_TILE_M 256
+#endif
+using Tile128 = Cfg<128, 2, 4, 3>;
+using Tile256 = Cfg<256, 4, 2, 2>;
+using TileCfg = std::conditional_t<MOE_GEMM1_TILE_M == 128, Tile128, Tile256>;
+static_assert(TileCfg::BM <= kMaxBM, "scale table padding covers one tile");
 
 }  // namespace
 
@@ -185,7 +408,7 @@ extern "C" moe_status moe_grouped_gemm1_workspace(const moe_dims* dims, int32_t 
     moe_status st = moe::load_dims(dims, &d, true);
     if (st != MOE_OK) return st;
     if (!bytes || n < 128 || n % 128 != 0) return MOE_ERR_INVALID_ARG;
-    *bytes = 0;
+    *bytes = (size_t)(d.H / BK) * (size_t)scale_ld_of(d.T * d.k) * sizeof(float);
     return MOE_OK;
 }
 
@@ -194,8 +417,6 @@ extern "C" moe_status moe_grouped_gemm1(const moe_dims* dims, int32_t n, const u
                                         const int32_t* expert_offsets, const int32_t* totals,
                                         const uint8_t* w_e4m3, const float* w_scale, uint16_t* y_bf16,
                                         void* ws, size_t ws_bytes, void* hip_stream) {
-    (void)ws;
-    (void)ws_bytes;
     (void)totals;
     moe::Dims d;
     moe_status st = moe::load_dims(dims, &d, true);
@@ -206,13 +427,25 @@ extern "C" moe_status moe_grouped_gemm1(const moe_dims* dims, int32_t n, const u
     if (!q_e4m3 || !q_scale || !row_slot || !expert_offsets || !w_e4m3 || !w_scale || !y_bf16)
         return MOE_ERR_INVALID_ARG;
     const int64_t rows_cap = d.T * d.k;
-    if (rows_cap * n >= ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
-    // upper bound of the tile count: sum over experts of ceil(rows/BM)
-    const int64_t max_tiles = ((rows_cap + BM - 1) / BM + d.L) * (n / BN);
-    const int grid = (int)std::min<int64_t>(max_tiles, 512);
-    hipLaunchKernelGGL(grouped_gemm1_kernel, dim3(grid), dim3(kThreads), 0,
-                       reinterpret_cast<hipStream_t>(hip_stream), q_e4m3, q_scale, row_slot,
-                       expert_offsets, w_e4m3, w_scale, y_bf16, (int)d.L, (int)n, (int)d.H, d.T,
-                       rows_cap);
+    // 32-bit offsets inside the kernel: slot rows of q, rows of one expert's weight
+    if (d.T * d.H >= ((int64_t)1 << 32) || (int64_t)n * d.H >= ((int64_t)1 << 31) ||
+        rows_cap * n >= ((int64_t)1 << 40))
+        return MOE_ERR_UNSUPPORTED;
+    const int64_t KB = d.H / BK;
+    const int64_t scale_ld = scale_ld_of(rows_cap);
+    if (!ws || ws_bytes < (size_t)(KB * scale_ld) * sizeof(float)) return MOE_ERR_WORKSPACE;
+    if (KB * scale_ld >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    int cus = cu_count();
+    if (cus <= 0) return MOE_ERR_HIP;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+    float* row_scale = reinterpret_cast<float*>(ws);
+    const int ggrid = (int)std::min<int64_t>((rows_cap + 255) / 256, 2048);
+    hipLaunchKernelGGL(gather_row_scales_kernel, dim3(ggrid), dim3(256), 0, stream, q_scale, row_slot,
+                       expert_offsets, (int)d.L, (int)KB, d.T, rows_cap, scale_ld, row_scale);
+    if ((st = moe::launch_status()) != MOE_OK) return st;
+    const int grid = ((cus + kXcds - 1) / kXcds) * kXcds;
+    hipLaunchKernelGGL((grouped_gemm1_kernel<TileCfg>), dim3(grid), dim3(TileCfg::kThreads), 0, stream,
+                       q_e4m3, row_scale, row_slot, expert_offsets, w_e4m3, w_scale, y_bf16, (int)d.L,
+                       (int)n, (int)d.H, d.T, rows_cap, scale_ld);
     return moe::launch_status();
 }

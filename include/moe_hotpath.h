@@ -132,7 +132,8 @@ moe_status moe_quant_dispatch(const moe_dims* dims, const uint16_t* x_bf16,
                               const int32_t* slot_tok, const int32_t* totals,
                               uint8_t* q_e4m3, float* q_scale, void* hip_stream);
 
-/* Workspace bytes moe_grouped_gemm1 needs (host-only; currently 0). */
+/* Workspace bytes moe_grouped_gemm1 needs (host-only): a K-block-major table of
+ * the rows' activation scales, (H/128) x (rows_cap + 128, rounded up to 64) floats. */
 moe_status moe_grouped_gemm1_workspace(const moe_dims* dims, int32_t n, size_t* bytes);
 
 /*
@@ -151,6 +152,8 @@ moe_status moe_grouped_gemm1_workspace(const moe_dims* dims, int32_t n, size_t* 
  *              element (h, c) of the logical [H, n] weight at [le, c, h]);
  *      w_scale float32 [L, n/128, H/128]  one scale per 128x128 block.
  * Out: y_bf16 uint16 (bf16 bits) [rows_cap, n]; rows past R are not written.
+ * ws: device workspace of at least moe_grouped_gemm1_workspace bytes (its
+ * contents need no initialisation; the call rewrites what it reads).
  * n must be a positive multiple of 128.  Row ids outside [0, T) read as zero
  * rows (they cannot come from step 1).
  */
