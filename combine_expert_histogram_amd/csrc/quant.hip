@@ -13,13 +13,15 @@
 // their send buffer interleaved payload and scales).
 //
 // Bit-exactness: the definition is e4m3(x / s) with an IEEE division.  The
-// kernel computes w = x * (1/s) (both roundings to nearest) and uses it
-// whenever w is not within a few fp32 ulps of an e4m3 rounding tie: then x/s
-// and w round to the same code.  The rare near-tie elements redo the IEEE
-// division.  Bound: 1/s and the product each carry <= 2^-24 relative error,
-// so |w - x/s| <= 2 ulp(x/s); the correctly rounded quotient is within 0.5 ulp
-// of x/s; the test window is +-8 ulp (normal range) or 2^-16 of the 2^-9 code
-// spacing (subnormal range, where the error is < 2^-19 of it).
+// kernel computes w = x * (1/s) (both roundings to nearest) and encodes w with
+// the hardware conversion (v_cvt_pk_fp8_f32: OCP e4m3, round to nearest even;
+// every |w| here is below the 464 rounding boundary, so no saturation case
+// arises), unless w lies within 8 fp32 ulps of an e4m3 rounding tie, or in the
+// e4m3 subnormal range (|w| < 2^-6, nonzero): such elements (rare; the lane
+// takes one divergent branch) redo the IEEE division x / s.  Bound: 1/s and
+// the product each carry <= 2^-24 relative error, so |w - x/s| <= 2 ulp(x/s),
+// and the correctly rounded quotient is within 0.5 ulp of x/s, so outside the
+// window both round to the same code.
 #include "common.h"
 
 namespace {
@@ -27,6 +29,8 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / MOE_WAVE;
 constexpr uint32_t kMinNormalBits = 0x3C800000u;   // 2^-6, smallest e4m3 normal
+
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t v) {
@@ -42,35 +46,20 @@ __device__ __forceinline__ uint32_t group8_max(uint32_t v) {
     return v;
 }
 
-// OCP e4m3 code of a finite fp32 value, round to nearest even, saturate at 448.
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-    const uint32_t b = __float_as_uint(v);
-    const uint32_t ab = b & 0x7FFFFFFFu;
-    const uint32_t sgn = (b >> 24) & 0x80u;
-    // normal range: drop 20 mantissa bits with round-to-nearest-even, rebias 127 -> 7
-    const uint32_t rb = ab + 0x7FFFFu + ((ab >> 20) & 1u);
-    const uint32_t cn = min((rb >> 20) - (120u << 3), 0x7Eu);
-    // subnormal range: multiples of 2^-9 (a count of 8 is the smallest normal)
-    const uint32_t cs = (uint32_t)rintf(__uint_as_float(ab) * 512.0f);
-    return (ab >= kMinNormalBits ? cn : cs) | sgn;
+// True when w might round differently from the IEEE quotient: within 8 ulps
+// of an e4m3 rounding tie in the normal range, or a nonzero e4m3 subnormal.
+__device__ __forceinline__ bool needs_exact(float w) {
+    const uint32_t ab = __float_as_uint(w) & 0x7FFFFFFFu;
+    const bool tie = ((ab & 0xFFFFFu) - 0x7FFF8u) < 16u;
+    const bool sub = (ab - 1u) < (kMinNormalBits - 1u);
+    return tie | sub;
 }
 
-// True when v is close enough to an e4m3 rounding tie that an approximate
-// quotient might round differently from the IEEE quotient.
-__device__ __forceinline__ bool near_tie(float v) {
-    const uint32_t ab = __float_as_uint(v) & 0x7FFFFFFFu;
-    const bool nn = ((ab & 0xFFFFFu) - 0x7FFF8u) < 16u;
-    const float t = __uint_as_float(ab) * 512.0f;
-    const bool ns = fabsf(t - floorf(t) - 0.5f) < 1.52587890625e-05f;   // 2^-16
-    return ab >= kMinNormalBits ? nn : ns;
-}
-
-__device__ __forceinline__ uint32_t quant_pair(uint32_t word, float r, float s, bool exact) {
-    float x0 = moe::bf16_lo(word), x1 = moe::bf16_hi(word);
-    float w0 = __fmul_rn(x0, r), w1 = __fmul_rn(x1, r);
-    if (exact || near_tie(w0)) w0 = x0 / s;
-    if (exact || near_tie(w1)) w1 = x1 / s;
-    return e4m3_code(w0) | (e4m3_code(w1) << 8);
+// four e4m3 codes of (a, b, c, d), hardware round to nearest even
+__device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
+    int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+    return (uint32_t)v;
 }
 
 __global__ void __launch_bounds__(kBlock)
@@ -98,24 +87,42 @@ quant_dispatch_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict_
                 v1 = __builtin_nontemporal_load(src + blk * 16 + sub * 2 + 1);
             }
             const uint32_t wv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-            uint32_t m = 0;
+            // |max| of the 16 bf16 values (packed 16-bit integer max of the magnitudes)
+            u16x2 m2 = {0, 0};
 #pragma unroll
-            for (int i = 0; i < 8; ++i) m = max(m, max(wv[i] & 0x7FFFu, (wv[i] >> 16) & 0x7FFFu));
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t a = wv[i] & 0x7FFF7FFFu;
+                m2 = __builtin_elementwise_max(m2, *reinterpret_cast<const u16x2*>(&a));
+            }
+            uint32_t m = max((uint32_t)m2.x, (uint32_t)m2.y);
             m = group8_max(m);
             const float amax = __uint_as_float(m << 16);
             const float s = amax / 448.0f;
             const float r = 1.0f / s;
-            // a zero block stores zeros; a scale too small for 1/s to be finite
-            // takes the exact division for every element
             const bool zero = m == 0;
-            const bool exact = !(r <= 3.0e38f);
+            // a scale too small for 1/s to be finite takes the exact division throughout
+            const bool all_exact = !(r <= 3.0e38f);
+            float xv[16], w[16];
+            bool slow = all_exact;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                xv[2 * i] = moe::bf16_lo(wv[i]);
+                xv[2 * i + 1] = moe::bf16_hi(wv[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                w[i] = __fmul_rn(xv[i], r);
+                slow |= needs_exact(w[i]);
+            }
+            if (slow) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (all_exact || needs_exact(w[i])) w[i] = xv[i] / s;
+            }
             uint32_t out[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t lo = quant_pair(wv[2 * i], r, s, exact);
-                const uint32_t hi = quant_pair(wv[2 * i + 1], r, s, exact);
-                out[i] = zero ? 0u : (lo | (hi << 16));
-            }
+            for (int i = 0; i < 4; ++i)
+                out[i] = zero ? 0u : cvt4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
             if (act) {
                 dst[blk * 8 + sub] = moe::u32x4{out[0], out[1], out[2], out[3]};
                 if (sub == 0) sdst[blk] = zero ? 0.0f : s;

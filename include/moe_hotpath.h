@@ -133,7 +133,9 @@ moe_status moe_quant_dispatch(const moe_dims* dims, const uint16_t* x_bf16,
                               uint8_t* q_e4m3, float* q_scale, void* hip_stream);
 
 /* Workspace bytes moe_grouped_gemm1 needs (host-only): a K-block-major table of
- * the rows' activation scales, (H/128) x (rows_cap + 128, rounded up to 64) floats. */
+ * the rows' activation scales, (H/128) x (rows_cap + 256, rounded up to 64) floats
+ * (padded to 256 B), then 16 B tile descriptors, (1 + (rows_cap/128 + L) *
+ * ceil(n/256)) of them.  Both are rewritten by every call. */
 moe_status moe_grouped_gemm1_workspace(const moe_dims* dims, int32_t n, size_t* bytes);
 
 /*

@@ -52,8 +52,10 @@ def test_capacity_and_workspace(L):
     assert b.moe_capacity(d) == (16384 * 8, 16384)
     ws = b.moe_route_layout_workspace(d)
     assert ws > 0 and ws % 256 == 0
-    # the row-scale table: H/128 K blocks x (rows_cap + one 256-row tile, 64-aligned) floats
-    assert b.moe_grouped_gemm1_workspace(d, 4096) == 56 * ((16384 * 8 + 256 + 63) // 64 * 64) * 4
+    # the row-scale table (H/128 K blocks x (rows_cap + one 256-row tile, 64-aligned) floats,
+    # 256 B aligned), then 16 B tile descriptors: one count + (rows_cap/128 + L) x (n/256)
+    table = (56 * ((16384 * 8 + 256 + 63) // 64 * 64) * 4 + 255) // 256 * 256
+    assert b.moe_grouped_gemm1_workspace(d, 4096) == table + (1 + (16384 * 8 // 128 + 32) * 16) * 16
     # the full-expert layout used by the combine
     assert b.moe_route_layout_workspace(b.Dims(S=8, Ts=2048, k=8, E=256, e0=0, L=256)) > 0
 
