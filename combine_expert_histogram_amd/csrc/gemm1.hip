@@ -231,15 +231,21 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const float* __restrict__ ro
                 af[i] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
                 f[i] = Ss[row] * sw;
             }
-            v4f pp[MI];
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
+            // B fragment of column group j; group j+1's is read before group j's MFMAs
+            auto read_b = [&](int j) __attribute__((always_inline)) {
                 const int col = wn * CW + j * 16 + (lane & 15);
                 const int c0 = (lane >> 4) * 2;
                 const int sw_c = (col & 7) ^ ((col >> 3) & 1);
                 const u32x4 b0 = *reinterpret_cast<const u32x4*>(Bs + col * BK + ((c0 ^ sw_c) << 4));
                 const u32x4 b1 = *reinterpret_cast<const u32x4*>(Bs + col * BK + (((c0 + 1) ^ sw_c) << 4));
-                const v8i bf = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+                return v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+            };
+            v4f pp[MI];
+            v8i bnext = read_b(0);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const v8i bf = bnext;
+                if (j + 1 < NJ) bnext = read_b(j + 1);
                 if constexpr (C::LAG < 0) {
 #pragma unroll
                     for (int i = 0; i < MI; ++i) {
