@@ -4,9 +4,13 @@
 // "each token read and quantised once"; "How it works now": every lane stores
 // one contiguous 16 B, 1 KiB per wavefront store instruction).
 //
-// Mapping: one wavefront per slot row; a pass covers 1024 hidden elements =
-// 8 blocks of 128; lane l takes 16 consecutive elements (two 16 B loads) of
-// block l/8, so a block is 8 adjacent lanes and its |max| is three DPP steps.
+// Mapping: one wavefront per half slot row (two work items per row, so the
+// last round of work items is not left mostly empty); a pass covers 1024
+// hidden elements = 8 blocks of 128; lane l takes 16 consecutive elements (two
+// 16 B loads) of block l/8, so a block is 8 adjacent lanes and its |max| is
+// three DPP steps.  The next pass's loads are issued before this pass's
+// arithmetic.  The activation rows are read with ordinary loads and the codes
+// written with non-temporal stores (measured best of the four combinations).
 // Because slot rows are dense and row-major, lane l's 16 codes land in bytes
 // [16l, 16l+16) of the pass: the wavefront's store is one contiguous 1 KiB
 // without an LDS round trip (the pages needed an LDS swizzle for that because
@@ -28,6 +32,9 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / MOE_WAVE;
+// pieces per slot row: with about one row per resident wavefront, whole rows
+// leave a second, mostly empty round of rows at the end
+constexpr int kSplit = 2;
 constexpr uint32_t kMinNormalBits = 0x3C800000u;   // 2^-6, smallest e4m3 normal
 
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
@@ -71,21 +78,32 @@ quant_dispatch_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict_
     const int sub = lane & 7;                    // 16-element piece within a block
     const int nblk = H / 128;
     const int64_t nwaves = (int64_t)gridDim.x * kWaves;
-    for (int64_t u = (int64_t)blockIdx.x * kWaves + threadIdx.x / MOE_WAVE; u < U; u += nwaves) {
+    // work item = one of kSplit pieces of a slot row (pieces of whole 8-block passes)
+    const int per = ((nblk + 8 * kSplit - 1) / (8 * kSplit)) * 8;
+    for (int64_t it = (int64_t)blockIdx.x * kWaves + threadIdx.x / MOE_WAVE; it < U * kSplit; it += nwaves) {
+        const int64_t u = it / kSplit;
+        const int b0 = (int)(it - u * kSplit) * per;
+        const int b1 = min(nblk, b0 + per);
+        if (b0 >= b1) continue;
         const int g = slot_tok[u];
         if ((uint64_t)g >= (uint64_t)T) continue;           // cannot come from the layout
         const moe::u32x4* src = reinterpret_cast<const moe::u32x4*>(x + (int64_t)g * H);
         moe::u32x4* dst = reinterpret_cast<moe::u32x4*>(q + u * H);
         float* sdst = q_scale + u * nblk;
-#pragma unroll 2
-        for (int cb = 0; cb < nblk; cb += 8) {
+        // software pipeline: the next pass's two loads are issued before this pass's
+        // arithmetic (addresses past the row's last block re-read that block)
+        auto load = [&](int cb, moe::u32x4& a, moe::u32x4& b) __attribute__((always_inline)) {
+            const int blk = min(cb + (lane >> 3), b1 - 1);
+            a = src[blk * 16 + sub * 2];
+            b = src[blk * 16 + sub * 2 + 1];
+        };
+        moe::u32x4 n0, n1;
+        load(b0, n0, n1);
+        for (int cb = b0; cb < b1; cb += 8) {
             const int blk = cb + (lane >> 3);
-            const bool act = blk < nblk;
-            moe::u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = v0;
-            if (act) {
-                v0 = __builtin_nontemporal_load(src + blk * 16 + sub * 2);
-                v1 = __builtin_nontemporal_load(src + blk * 16 + sub * 2 + 1);
-            }
+            const bool act = blk < b1;
+            const moe::u32x4 v0 = n0, v1 = n1;
+            if (cb + 8 < b1) load(cb + 8, n0, n1);
             const uint32_t wv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
             // |max| of the 16 bf16 values (packed 16-bit integer max of the magnitudes)
             u16x2 m2 = {0, 0};
@@ -124,7 +142,7 @@ quant_dispatch_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict_
             for (int i = 0; i < 4; ++i)
                 out[i] = zero ? 0u : cvt4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
             if (act) {
-                dst[blk * 8 + sub] = moe::u32x4{out[0], out[1], out[2], out[3]};
+                __builtin_nontemporal_store(moe::u32x4{out[0], out[1], out[2], out[3]}, dst + blk * 8 + sub);
                 if (sub == 0) sdst[blk] = zero ? 0.0f : s;
             }
         }
@@ -142,7 +160,7 @@ extern "C" moe_status moe_quant_dispatch(const moe_dims* dims, const uint16_t* x
     if (d.T == 0) return MOE_OK;
     if (!x_bf16 || !slot_tok || !totals || !q_e4m3 || !q_scale) return MOE_ERR_INVALID_ARG;
     if (d.T * d.H >= ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
-    const int64_t waves = d.T;                                   // one per slot (slots_cap = T)
+    const int64_t waves = d.T * kSplit;                          // one per row piece (slots_cap = T)
     const int grid = (int)std::min<int64_t>((waves + kWaves - 1) / kWaves, 16384);
     hipLaunchKernelGGL(quant_dispatch_kernel, dim3(grid), dim3(kBlock), 0,
                        reinterpret_cast<hipStream_t>(hip_stream), x_bf16, slot_tok, totals, d.T,
