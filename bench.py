@@ -191,13 +191,15 @@ def main():
                                                                 "traffic")}
     roof["kernel"] = dominant
 
-    if args.copy_calib:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
+    pct = lambda v, p: float(np.percentile(v, p))
+    stage1_all = [sum(per[n][i] for n in ("layout_local", "quant", "gemm1")) for i in range(args.steps)]
+    spread = {n: {"p10": round(pct(per[n], 10), 2), "p90": round(pct(per[n], 90), 2)} for n in names}
+    spread["stage1"] = {"p10": round(pct(stage1_all, 10), 2), "p90": round(pct(stage1_all, 90), 2)}
+
+    # stage1 (layout -> quant -> GEMM1) captured once in a graph and replayed; the
+    # calls read their counts on the device, so the capture needs no host sync
+    graph = stage1_graph(torch, moe, d_loc, ids_d, x_d, wq_d, ws_d, lay, q, qs, y1, g_ws, w, R, U, args.steps)
+    ceil = ceilings(torch, moe, args.copy_calib)
 
     rec = {
         "metric": METRIC, "value": round(stage1, 2), "unit": "µs", "n_gpus": 1,
@@ -213,12 +215,93 @@ def main():
         "kernels_us_mean": {n: round(mean[n], 2) for n in names},
         "kernels": kernels,
         "roofline": roof,
+        "percentiles_us": spread,
+        "stage1_graph": graph,
+        "ceilings": ceil,
+        "fraction_of_measured_ceilings": {
+            "gemm1_vs_mfma_loop": round(gemm_tflops / ceil["mfma_fp8_tflops"], 4),
+            "dispatch_combine_vs_copy": round(hbm_gbs / ceil["copy_gbs"], 4)},
     }
 
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, ids, wts, lay, lay_all, q, qs, y1, out, Y_d, R, U, stage1)
 
     print(json.dumps(rec), flush=True)
+
+
+def stage1_graph(torch, moe, d, ids_d, x_d, wq_d, ws_d, lay, q, qs, y1, g_ws, w, R, U, steps):
+    """Captures layout -> quant -> GEMM1 into one graph (all buffers preallocated),
+    replays it `steps` times back to back (events between the replays, on the
+    replay stream) and checks the graph's outputs against the eager step's."""
+    ref_lay = {k: v.clone() for k, v in lay.items() if k != "ws"}
+    ref_q, ref_qs, ref_y = q[:U].clone(), qs[:U].clone(), y1[:R].clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        moe.route_layout(d, ids_d, lay)                      # warm the stream before capture
+        moe.quant_dispatch(d, x_d, lay, q, qs)
+        moe.grouped_gemm1(d, w.N, q, qs, lay, wq_d, ws_d, y1, g_ws)
+        s.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            moe.route_layout(d, ids_d, lay)
+            moe.quant_dispatch(d, x_d, lay, q, qs)
+            moe.grouped_gemm1(d, w.N, q, qs, lay, wq_d, ws_d, y1, g_ws)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    # back to back, like the eager steps: an event between consecutive replays
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    with torch.cuda.stream(s):
+        for i in range(steps):
+            ev[i].record(s)
+            g.replay()
+        ev[steps].record(s)
+    torch.cuda.synchronize()
+    times = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps)]
+    same = (all(torch.equal(lay[k], v) for k, v in ref_lay.items()) and torch.equal(q[:U], ref_q)
+            and torch.equal(qs[:U], ref_qs) and torch.equal(y1[:R], ref_y))
+    return {"us_median": round(float(np.median(times)), 2), "us_p10": round(float(np.percentile(times, 10)), 2),
+            "us_p90": round(float(np.percentile(times, 90)), 2), "replays": steps, "matches_eager": bool(same)}
+
+
+def ceilings(torch, moe, copy_calib):
+    """What this GPU sustains in the same run: a 1 GiB device-to-device copy
+    (bytes read + written per second) and a loop of independent fp8 MFMAs."""
+    import ctypes
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    reps = 3 if copy_calib else 5
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    for i in range(reps):
+        e[i].record(); b.copy_(a)
+    e[reps].record(); torch.cuda.synchronize()
+    copy_us = float(np.median([e[i].elapsed_time(e[i + 1]) * 1e3 for i in range(reps)]))
+    del a, b
+    lib = ctypes.CDLL(os.path.join(ROOT, "combine_expert_histogram_amd", "libmoe_ceiling.so"))
+    lib.moe_ceiling_mfma_fp8.restype = ctypes.c_int
+    lib.moe_ceiling_mfma_fp8.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    grid = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(grid * 512, dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream()
+    iters = 4000
+    if lib.moe_ceiling_mfma_fp8(grid, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(st.cuda_stream)):
+        raise RuntimeError("MFMA ceiling launch failed")
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for i in range(3):
+        e[i].record(st)
+        lib.moe_ceiling_mfma_fp8(grid, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(st.cuda_stream))
+    e[3].record(st); torch.cuda.synchronize()
+    mfma_us = float(np.median([e[i].elapsed_time(e[i + 1]) * 1e3 for i in range(3)]))
+    flop = grid * 8 * iters * 16 * 65536
+    return {"copy_gbs": round(2 * (1 << 30) / (copy_us * 1e-6) / 1e9, 1),
+            "mfma_fp8_tflops": round(flop / (mfma_us * 1e-6) / 1e12, 1),
+            "mfma_fp8_frac_of_peak": round(flop / (mfma_us * 1e-6) / 1e12 / FP8_PEAK_TFLOPS, 4)}
 
 
 def cpu_baseline(w, ids, wts, lay, lay_all, q, qs, y1, out, Y_d, R, U, gpu_stage1_us):

@@ -1,4 +1,5 @@
-"""Builds libmoe_hotpath.so (gfx950) in-tree with hipcc.
+"""Builds libmoe_hotpath.so (gfx950) in-tree with hipcc, and libmoe_ceiling.so,
+the benchmark's MFMA-rate probe (not part of the hot path's C ABI).
 
 Usage: python -m combine_expert_histogram_amd.build
 """
@@ -15,6 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_hotpath.so")
 SOURCES = ["api.hip", "layout.hip", "quant.hip", "gemm1.hip", "combine.hip"]
+CEILING_LIB = os.path.join(PKG, "libmoe_ceiling.so")
+CEILING_SOURCES = ["ceiling.hip"]
 ARCH = "gfx950"
 
 
@@ -37,17 +40,22 @@ def flags() -> list[str]:
     ]
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
+def _link(sources: list[str], out: str, verbose: bool) -> str:
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = out + ".tmp"
     cmd = [hipcc(), *flags(), *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    _link(CEILING_SOURCES, CEILING_LIB, verbose)
+    return _link(SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":

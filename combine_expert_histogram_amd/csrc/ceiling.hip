@@ -1,0 +1,46 @@
+// Measurement aid, not part of the hot path's C ABI (built as a separate
+// library, libmoe_ceiling.so, loaded only by the benchmark): a kernel that does
+// nothing but fp8 MFMAs, so the benchmark can report the MFMA rate this chip
+// sustains in the same run next to the grouped GEMM1's rate.
+//
+// Each wavefront keeps 16 independent 16x16x128 fp8 MFMA accumulators and
+// runs `iters` rounds of 16 MFMAs (the operands vary with the lane and the
+// accumulators carry from round to round, so nothing can be hoisted); 8
+// wavefronts per workgroup, one workgroup per CU.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__global__ void __launch_bounds__(512) mfma_loop_kernel(int iters, float* out) {
+    const int lane = threadIdx.x;
+    const v8i a = {lane, lane * 3, 0x38383838, 0x30303030, lane ^ 0x55, 11, 13, lane * 5};
+    const v8i b = {lane * 7, 0x38383838, 2, 3, 0x28282828, 5, lane, 7};
+    v4f acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            acc[k] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[k], 0, 0, 0, 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+}  // namespace
+
+// Launches grid workgroups of 512 threads on `hip_stream`; `out` holds
+// grid * 512 floats.  FLOP per launch = grid * 8 * iters * 16 * 65536.
+// Returns 0, or -1 for bad arguments / a launch error.
+extern "C" int moe_ceiling_mfma_fp8(int grid, int iters, float* out, void* hip_stream) {
+    if (grid <= 0 || iters <= 0 || !out) return -1;
+    hipLaunchKernelGGL(mfma_loop_kernel, dim3(grid), dim3(512), 0, reinterpret_cast<hipStream_t>(hip_stream),
+                       iters, out);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
