@@ -67,6 +67,7 @@ constexpr int BN = 256, BK = 128;
 constexpr int kMaxL = 1024;
 constexpr int kXcds = 8;
 constexpr int kMinBM = 128;   // tile descriptors are sized for the smallest row tile
+constexpr int kPrepKb = 8;    // K blocks per row-scale gather work item
 
 #define GPTR(p) ((const void __attribute__((address_space(1)))*)(p))
 #define LPTR(p) ((void __attribute__((address_space(3)))*)(p))
@@ -379,12 +380,23 @@ gemm1_prep_kernel(const float* __restrict__ q_scale, const int32_t* __restrict__
     }
     int64_t R = expert_offsets[L];
     R = R < 0 ? 0 : (R > rows_cap ? rows_cap : R);
+    // work item = (row, group of kPrepKb K blocks); consecutive items are
+    // consecutive rows of one group, so every store instruction is contiguous
+    const int KG = (KB + kPrepKb - 1) / kPrepKb;
     const int64_t nthr = (int64_t)(gridDim.x - 1) * 256;
-    for (int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x; r < R; r += nthr) {
+    for (int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x; item < R * KG; item += nthr) {
+        const int kg = (int)(item / R);
+        const int64_t r = item - (int64_t)kg * R;
         const int s = row_slot[r];
         const bool ok = (uint64_t)s < (uint64_t)T;
         const float* src = q_scale + (int64_t)(ok ? s : 0) * KB;
-        for (int kb = 0; kb < KB; ++kb) out[kb * scale_ld + r] = ok ? src[kb] : 0.0f;
+        const int k0 = kg * kPrepKb;
+        float v[kPrepKb];
+#pragma unroll
+        for (int i = 0; i < kPrepKb; ++i) v[i] = (ok && k0 + i < KB) ? src[k0 + i] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < kPrepKb; ++i)
+            if (k0 + i < KB) out[(int64_t)(k0 + i) * scale_ld + r] = v[i];
     }
 }
 
@@ -463,7 +475,8 @@ extern "C" moe_status moe_grouped_gemm1(const moe_dims* dims, int32_t n, const u
     int4* tiles = reinterpret_cast<int4*>(static_cast<uint8_t*>(ws) + wl.table_bytes);
     const int NT = (int)((n + BN - 1) / BN);
     // gather workgroups plus the planning workgroup (the last one)
-    const int pgrid = (int)std::min<int64_t>((rows_cap + 255) / 256, 2048) + 1;
+    const int64_t KG = (KB + kPrepKb - 1) / kPrepKb;
+    const int pgrid = (int)std::min<int64_t>((rows_cap * KG + 255) / 256, 4096) + 1;
     hipLaunchKernelGGL((gemm1_prep_kernel<TileCfg::BM>), dim3(pgrid), dim3(256), 0, stream, q_scale, row_slot,
                        expert_offsets, (int)d.L, (int)KB, NT, d.T, rows_cap, wl.scale_ld, row_scale, tiles,
                        wl.tiles_cap);

@@ -38,6 +38,7 @@ constexpr int kMaxLocalExperts = 1024;
 struct Plan {
     int64_t CB = 64;   // tokens per chunk (one workgroup)
     int64_t NC = 0;    // chunks
+    int64_t NCp = 0;   // histogram row stride: NC rounded up to 4 (16 B rows)
     int64_t off_hist = 0, off_landed = 0, total_ints = 0;   // workspace, int32 units
 };
 
@@ -47,9 +48,10 @@ Plan make_plan(const Dims& d) {
     auto nchunks = [&](int64_t cb) { return (d.T + cb - 1) / cb; };
     while (nchunks(p.CB) * d.L > kHistTarget && p.CB < cap) p.CB *= 2;
     p.NC = nchunks(p.CB);
+    p.NCp = (p.NC + 3) & ~int64_t(3);
     auto al = [](int64_t v) { return (v + 63) & ~int64_t(63); };   // 256-byte alignment
     p.off_hist = 0;
-    p.off_landed = al(d.L * p.NC);
+    p.off_landed = al(d.L * p.NCp);
     p.total_ints = al(p.off_landed + p.NC);
     return p;
 }
@@ -83,7 +85,7 @@ __device__ __forceinline__ void wave_sync_lds() {
 // ------------------------------------------------------------------ count
 __global__ void __launch_bounds__(kBlock)
 layout_count_kernel(const int32_t* __restrict__ ids, int64_t T, int k, int e0, int L, int CB,
-                    int NC, int32_t* __restrict__ hist, int32_t* __restrict__ landed) {
+                    int NCp, int32_t* __restrict__ hist, int32_t* __restrict__ landed) {
     extern __shared__ __align__(16) unsigned char smem[];
     int* cnt = reinterpret_cast<int*>(smem);
     int* red = cnt + L;                                   // 16 ints
@@ -108,7 +110,7 @@ layout_count_kernel(const int32_t* __restrict__ ids, int64_t T, int k, int e0, i
     for (int i = tid; i < (int)(t1 - t0); i += kBlock) nl += flag[i];
     nl = moe::wave_sum(nl);
     if (tid % MOE_WAVE == 0) red[tid / MOE_WAVE] = nl;
-    for (int i = tid; i < L; i += kBlock) hist[(int64_t)i * NC + c] = cnt[i];
+    for (int i = tid; i < L; i += kBlock) hist[(int64_t)i * NCp + c] = cnt[i];
     __syncthreads();
     if (tid == 0) landed[c] = red[0] + red[1] + red[2] + red[3];
 }
@@ -116,7 +118,7 @@ layout_count_kernel(const int32_t* __restrict__ ids, int64_t T, int k, int e0, i
 // ------------------------------------------------------------------ place
 __global__ void __launch_bounds__(kBlock)
 layout_place_kernel(const int32_t* __restrict__ ids, int64_t T, int k, int e0, int L, int CB,
-                    int NC, int S, int64_t Ts, const int32_t* __restrict__ hist,
+                    int NC, int NCp, int S, int64_t Ts, const int32_t* __restrict__ hist,
                     const int32_t* __restrict__ landed, int32_t* __restrict__ expert_counts,
                     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ row_slot,
                     int32_t* __restrict__ row_assign, int32_t* __restrict__ assign_row,
@@ -150,28 +152,31 @@ layout_place_kernel(const int32_t* __restrict__ ids, int64_t T, int k, int e0, i
     if (tid < 16) misc[tid] = 0;
     __syncthreads();
 
-    // (1) prefix information from the histogram: each thread sums a
-    // contiguous run of the expert-major histogram, split at chunk c.
+    // (1) prefix information from the histogram: each thread takes whole experts
+    // and reads its expert's row (16 B loads, issued together) for the rows of
+    // all earlier chunks (A) and the expert's total (Tt)
     {
-        const int n = L * NC;
-        const int per = (n + kBlock - 1) / kBlock;
-        int i = tid * per;
-        const int i1 = min(n, i + per);
-        if (i < i1) {
-            int le = i / NC, cc = i - le * NC;
+        for (int le = tid; le < L; le += kBlock) {
+            const int4* row = reinterpret_cast<const int4*>(hist + (int64_t)le * NCp);
             int sa = 0, st = 0;
-            for (; i < i1; ++i) {
-                const int v = hist[i];
-                st += v;
-                if (cc < c) sa += v;
-                if (++cc == NC || i + 1 == i1) {
-                    if (sa) atomicAdd(&A[le], sa);
-                    if (st) atomicAdd(&Tt[le], st);
-                    sa = st = 0;
-                    cc = 0;
-                    ++le;
+            for (int q0 = 0; q0 < NCp / 4; q0 += 8) {
+                int4 v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[u] = q0 + u < NCp / 4 ? row[q0 + u] : int4{0, 0, 0, 0};
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int cc = (q0 + u) * 4;
+                    const int e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                    for (int z = 0; z < 4; ++z) {
+                        const int val = cc + z < NC ? e[z] : 0;     // stride padding is not written
+                        st += val;
+                        if (cc + z < c) sa += val;
+                    }
                 }
             }
+            A[le] = sa;
+            Tt[le] = st;
         }
         int lb = 0, lt = 0;
         for (int j = tid; j < NC; j += kBlock) {
@@ -341,7 +346,7 @@ extern "C" moe_status moe_route_layout(const moe_dims* dims, const int32_t* topk
         return MOE_ERR_INVALID_ARG;
     const Plan p = make_plan(d);
     if (!ws || ws_bytes < (size_t)p.total_ints * 4) return MOE_ERR_WORKSPACE;
-    if (p.NC * d.L >= INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    if (p.NCp * d.L >= INT32_MAX) return MOE_ERR_UNSUPPORTED;
     hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
     int32_t* w = reinterpret_cast<int32_t*>(ws);
     int32_t* hist = w + p.off_hist;
@@ -349,7 +354,7 @@ extern "C" moe_status moe_route_layout(const moe_dims* dims, const int32_t* topk
 
     if (p.NC > 0) {
         hipLaunchKernelGGL(layout_count_kernel, dim3((unsigned)p.NC), dim3(kBlock), count_lds(d, p),
-                           stream, topk_ids, d.T, (int)d.k, (int)d.e0, (int)d.L, (int)p.CB, (int)p.NC,
+                           stream, topk_ids, d.T, (int)d.k, (int)d.e0, (int)d.L, (int)p.CB, (int)p.NCp,
                            hist, landed);
         if ((st = moe::launch_status()) != MOE_OK) return st;
     }
@@ -357,7 +362,7 @@ extern "C" moe_status moe_route_layout(const moe_dims* dims, const int32_t* topk
     const unsigned grid = (unsigned)std::max<int64_t>(p.NC, 1);
     hipLaunchKernelGGL(layout_place_kernel, dim3(grid), dim3(kBlock), place_lds(d.L, p.CB).total,
                        stream, topk_ids, d.T, (int)d.k, (int)d.e0, (int)d.L, (int)p.CB, (int)p.NC,
-                       (int)d.S, d.Ts, hist, landed, expert_counts, expert_offsets, row_slot,
+                       (int)p.NCp, (int)d.S, d.Ts, hist, landed, expert_counts, expert_offsets, row_slot,
                        row_assign, assign_row, tok_slot, slot_tok, src_slot_offsets, totals);
     return moe::launch_status();
 }
