@@ -20,6 +20,10 @@ Each function is the plain definition of one step, written from the pages:
 * ``combine.combine`` - the top-k weighted combine back to token order
   (TilePipe "Communication Kernels": push combine; MegaMoE PR "What": stage2 +
   combine).
+* ``mx.quant_dispatch`` / ``mx.grouped_gemm1`` - the same quant and GEMM1 with
+  the pages' own scale format: power-of-two (e8m0) scales per group of 32 K
+  elements, packed four per dword (MegaMoE PR, "Where we stand" and commit
+  "ready-first / quant-lds-store").
 * ``fp8`` / ``bf16`` - the OCP FP8 E4M3 encoding and bf16 rounding the steps
   rely on.
 

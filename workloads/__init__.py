@@ -210,3 +210,47 @@ def expert_outputs(w: Workload, rows: int | None = None, width: int | None = Non
 
 def sha256(a: np.ndarray) -> str:
     return hashlib.sha256(np.ascontiguousarray(a).view(np.uint8)).hexdigest()
+
+
+def weights_mx(w: Workload, experts: range | None = None):
+    """GEMM1 weights in the MX-style format: the same fp32 N(0, 0.02) -> bf16
+    draws as ``weights``, quantised per column n and group of 32 consecutive K
+    elements with a power-of-two scale: E = ceil(log2(group |max| / 448))
+    (the fp32 quotient's binary exponent; an all-zero group gets E = -127),
+    payload = e4m3(value * 2^-E) (torch's float8_e4m3fn cast; exact scaling,
+    every magnitude <= 448).  The e8m0 codes E + 127 are packed four per
+    uint32 (group 4kb+g in byte g) and stored K-block-major.
+
+    Returns (w_e4m3 uint8 [L', N, H], w_scale uint32 [L', H/128, N]).
+    """
+    import torch
+    L, N, H = w.L, w.N, w.H
+    experts = range(L) if experts is None else experts
+    seeds = _stream(w.seed, "weights").spawn(L)
+    q = np.empty((len(experts), N, H), dtype=np.uint8)
+    sc = np.empty((len(experts), H // 128, N), dtype=np.uint32)
+
+    def one(i_le):
+        i, le = i_le
+        g = np.random.default_rng(seeds[le])
+        wf = g.standard_normal(size=(N, H), dtype=np.float32)
+        wf *= np.float32(0.02)
+        t = torch.from_numpy(wf).to(torch.bfloat16).to(torch.float32).view(N, H // 32, 32)
+        amax = t.abs().amax(dim=2)
+        m, e = torch.frexp(amax / torch.tensor(448.0, dtype=torch.float32))
+        E = torch.where(m == 0.5, e - 1, e).to(torch.int64)
+        E = torch.where(amax == 0, torch.full_like(E, -127), E).clamp(-127, 127)
+        v = torch.ldexp(t.to(torch.float64), (-E)[:, :, None].to(torch.float64)).to(torch.float32)
+        q[i] = v.to(torch.float8_e4m3fn).view(torch.uint8).reshape(N, H).numpy()
+        c = (E + 127).to(torch.int64).view(N, H // 128, 4)
+        packed = c[..., 0] | (c[..., 1] << 8) | (c[..., 2] << 16) | (c[..., 3] << 24)
+        sc[i] = packed.t().numpy().astype(np.uint32)
+
+    items = list(enumerate(experts))
+    if len(items) <= 1:
+        for it in items:
+            one(it)
+    else:
+        with _cf.ThreadPoolExecutor(min(_threads(), 8)) as ex:
+            list(ex.map(one, items))
+    return q, sc
