@@ -22,7 +22,8 @@ _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_WORKSPACE",
 
 # every symbol include/moe_hotpath.h declares
 EXPORTS = ("moe_status_string", "moe_capacity", "moe_route_layout_workspace", "moe_route_layout",
-           "moe_quant_dispatch", "moe_grouped_gemm1_workspace", "moe_grouped_gemm1", "moe_combine")
+           "moe_quant_dispatch", "moe_grouped_gemm1_workspace", "moe_grouped_gemm1",
+           "moe_quant_dispatch_mx", "moe_grouped_gemm1_mx", "moe_combine")
 
 
 class MoeError(RuntimeError):
@@ -77,6 +78,8 @@ def lib() -> ctypes.CDLL:
             "moe_quant_dispatch": (I32, [D, P, P, P, P, P, P]),
             "moe_grouped_gemm1_workspace": (I32, [D, I32, ctypes.POINTER(SZ)]),
             "moe_grouped_gemm1": (I32, [D, I32] + [P] * 8 + [P, SZ, P]),
+            "moe_quant_dispatch_mx": (I32, [D, P, P, P, P, P, P]),
+            "moe_grouped_gemm1_mx": (I32, [D, I32] + [P] * 7 + [P, SZ, P]),
             "moe_combine": (I32, [D, I32, P, I64, P, P, P, P]),
         }
         for name, (res, args) in sig.items():
@@ -177,6 +180,34 @@ def moe_grouped_gemm1(d: Dims, n: int, q_e4m3, q_scale, row_slot, expert_offsets
     _check("moe_grouped_gemm1", st)
 
 
+def _u32(t, name, n):
+    if t is not None and t.dtype not in (torch.int32, torch.uint32):
+        raise ValueError(f"{name} must be a 32-bit integer tensor (packed e8m0 codes)")
+    return _ptr(t, name, 4 * n)
+
+
+def moe_quant_dispatch_mx(d: Dims, x_bf16, slot_tok, totals, q_e4m3, q_scale) -> None:
+    T, H = d.T, d.H
+    st = lib().moe_quant_dispatch_mx(
+        ctypes.byref(d.c()), _ptr(x_bf16, "x_bf16", 2 * T * H, 2), _i32(slot_tok, "slot_tok", T),
+        _i32(totals, "totals", 2), _ptr(q_e4m3, "q_e4m3", T * H, 1),
+        _u32(q_scale, "q_scale", T * (H // 128)), _stream())
+    _check("moe_quant_dispatch_mx", st)
+
+
+def moe_grouped_gemm1_mx(d: Dims, n: int, q_e4m3, q_scale, row_slot, expert_offsets,
+                         w_e4m3, w_scale, y_bf16, ws=None) -> None:
+    T, H, L = d.T, d.H, d.L
+    rows_cap = T * d.k
+    st = lib().moe_grouped_gemm1_mx(
+        ctypes.byref(d.c()), n, _ptr(q_e4m3, "q_e4m3", T * H, 1), _u32(q_scale, "q_scale", T * (H // 128)),
+        _i32(row_slot, "row_slot", rows_cap), _i32(expert_offsets, "expert_offsets", L + 1),
+        _ptr(w_e4m3, "w_e4m3", L * n * H, 1), _u32(w_scale, "w_scale", L * (H // 128) * n),
+        _ptr(y_bf16, "y_bf16", 2 * rows_cap * n, 2), _ptr(ws, "ws", moe_grouped_gemm1_workspace(d, n)),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream())
+    _check("moe_grouped_gemm1_mx", st)
+
+
 def moe_combine(d: Dims, width: int, y_bf16, assign_row, topk_w, out_bf16) -> None:
     T, k = d.T, d.k
     y_rows = 0 if y_bf16 is None else y_bf16.numel() // max(width, 1)
@@ -228,6 +259,22 @@ def grouped_gemm1(d: Dims, n: int, q, q_scale, lay: dict, w_e4m3, w_scale, y=Non
     ws = alloc_gemm1_workspace(d, n, q.device) if ws is None else ws
     moe_grouped_gemm1(d, n, q, q_scale, lay["row_slot"], lay["expert_offsets"], lay["totals"],
                       w_e4m3, w_scale, y, ws)
+    return y
+
+
+def quant_dispatch_mx(d: Dims, x_bf16, lay: dict, q=None, q_scale=None):
+    dev = x_bf16.device
+    q = torch.empty((max(d.T, 1), d.H), dtype=torch.uint8, device=dev) if q is None else q
+    q_scale = (torch.empty((max(d.T, 1), d.H // 128), dtype=torch.int32, device=dev)
+               if q_scale is None else q_scale)
+    moe_quant_dispatch_mx(d, x_bf16, lay["slot_tok"], lay["totals"], q, q_scale)
+    return q, q_scale
+
+
+def grouped_gemm1_mx(d: Dims, n: int, q, q_scale, lay: dict, w_e4m3, w_scale, y=None, ws=None):
+    y = torch.empty((max(d.T * d.k, 1), n), dtype=torch.bfloat16, device=q.device) if y is None else y
+    ws = alloc_gemm1_workspace(d, n, q.device) if ws is None else ws
+    moe_grouped_gemm1_mx(d, n, q, q_scale, lay["row_slot"], lay["expert_offsets"], w_e4m3, w_scale, y, ws)
     return y
 
 

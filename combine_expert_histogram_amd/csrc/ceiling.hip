@@ -6,7 +6,8 @@
 // Each wavefront keeps 16 independent 16x16x128 fp8 MFMA accumulators and
 // runs `iters` rounds of 16 MFMAs (the operands vary with the lane and the
 // accumulators carry from round to round, so nothing can be hoisted); 8
-// wavefronts per workgroup, one workgroup per CU.
+// wavefronts per workgroup, one workgroup per CU.  The scaled variant passes
+// per-lane e8m0 block scales (codes 126 .. 129) as the MX GEMM1 does.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -15,8 +16,10 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
+template <bool SCALED>
 __global__ void __launch_bounds__(512) mfma_loop_kernel(int iters, float* out) {
     const int lane = threadIdx.x;
+    const int sa = SCALED ? 126 + (lane & 3) : 0, sb = SCALED ? 126 + ((lane >> 2) & 3) : 0;
     const v8i a = {lane, lane * 3, 0x38383838, 0x30303030, lane ^ 0x55, 11, 13, lane * 5};
     const v8i b = {lane * 7, 0x38383838, 2, 3, 0x28282828, 5, lane, 7};
     v4f acc[16];
@@ -25,7 +28,7 @@ __global__ void __launch_bounds__(512) mfma_loop_kernel(int iters, float* out) {
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
         for (int k = 0; k < 16; ++k)
-            acc[k] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[k], 0, 0, 0, 0, 0, 0);
+            acc[k] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[k], 0, 0, 0, sa, 0, sb);
     }
     float s = 0.f;
 #pragma unroll
@@ -40,7 +43,15 @@ __global__ void __launch_bounds__(512) mfma_loop_kernel(int iters, float* out) {
 // Returns 0, or -1 for bad arguments / a launch error.
 extern "C" int moe_ceiling_mfma_fp8(int grid, int iters, float* out, void* hip_stream) {
     if (grid <= 0 || iters <= 0 || !out) return -1;
-    hipLaunchKernelGGL(mfma_loop_kernel, dim3(grid), dim3(512), 0, reinterpret_cast<hipStream_t>(hip_stream),
-                       iters, out);
+    hipLaunchKernelGGL(mfma_loop_kernel<false>, dim3(grid), dim3(512), 0,
+                       reinterpret_cast<hipStream_t>(hip_stream), iters, out);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// The same with nonzero per-lane e8m0 scales (the MX GEMM1's instruction form).
+extern "C" int moe_ceiling_mfma_fp8_scaled(int grid, int iters, float* out, void* hip_stream) {
+    if (grid <= 0 || iters <= 0 || !out) return -1;
+    hipLaunchKernelGGL(mfma_loop_kernel<true>, dim3(grid), dim3(512), 0,
+                       reinterpret_cast<hipStream_t>(hip_stream), iters, out);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -92,7 +92,7 @@ struct Cfg {
     static constexpr int kCompute = WM * WN, kWaves = kCompute + NLW, kThreads = kWaves * MOE_WAVE;
     static constexpr int RW = BM / WM, CW = BN / WN, MI = RW / 16, NJ = CW / 16;
     static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
-    static constexpr int S_BYTES = NLW * 256;                 // loader l: row scales of rows 64l..64l+63
+    static constexpr int S_BYTES = NLW * 256;                 // row scales of rows 0 .. 64 NLW - 1
     static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
     static constexpr int A_LOADS = A_BYTES / (1024 * NLW), B_LOADS = B_BYTES / (1024 * NLW);
     static constexpr int NLD = A_LOADS + B_LOADS + 1;         // loads per loader per stage
@@ -104,15 +104,33 @@ struct Cfg {
     static_assert(LAG >= -1 && LAG <= 1, "fold placement");
 };
 
-template <class C>
+// MX: the operands carry e8m0 scales per 32 K elements (packed four per dword:
+// rows' dwords gathered into the row-scale table, the weights' dwords stored
+// [L, H/128, N]); they ride in the MFMA's block-scale operands, so the K blocks
+// accumulate in the MFMA itself and there is no fold.
+template <class C, bool MX>
 __global__ void __launch_bounds__(C::kThreads, 1)
-grouped_gemm1_kernel(const uint8_t* __restrict__ q, const float* __restrict__ row_scale,
-                        const int4* __restrict__ tiles, const int32_t* __restrict__ row_slot,
-                        const uint8_t* __restrict__ w, const float* __restrict__ w_scale,
-                        uint16_t* __restrict__ y, int N, int H, int64_t T, int64_t scale_ld) {
+grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__ row_scale,
+                     const int4* __restrict__ tiles, const int32_t* __restrict__ row_slot,
+                     const uint8_t* __restrict__ w, const void* __restrict__ w_scale_v,
+                     uint16_t* __restrict__ y, int N, int H, int64_t T, int64_t scale_ld) {
+    // fp32 path: one float per (expert, 128 columns, K block), [L, N/128, H/128];
+    // MX path: packed e8m0 codes per (expert, K block, column), [L, H/128, N]
+    const float* w_scale = static_cast<const float*>(w_scale_v);
+    const uint32_t* w_scale_mx = static_cast<const uint32_t*>(w_scale_v);
     constexpr int BM = C::BM, MI = C::MI, NJ = C::NJ, RW = C::RW, CW = C::CW, WN = C::WN;
-    constexpr int A_BYTES = C::A_BYTES, B_BYTES = C::B_BYTES, STAGE = C::STAGE, NSTAGE = C::NSTAGE;
-    constexpr int A_LOADS = C::A_LOADS, B_LOADS = C::B_LOADS, NLD = C::NLD;
+    constexpr int A_BYTES = C::A_BYTES, B_BYTES = C::B_BYTES, NSTAGE = C::NSTAGE;
+    // MX stages also hold the columns' scale dwords (1 KiB: BN columns)
+    constexpr int STAGE = C::STAGE + (MX ? C::NLW * 256 : 0);
+    constexpr int A_LOADS = C::A_LOADS, B_LOADS = C::B_LOADS;
+    // Per stage each loader issues its A and B loads plus at most one scale load:
+    // loaders lw < BM/64 bring rows lw*64 .. lw*64+63's scales (4 B a lane), and
+    // in MX mode loader SB_LOADER brings the BN columns' scale dwords (16 B a lane)
+    constexpr int NSA = C::BM / 64, SB_LOADER = NSA;
+    constexpr int NLD = A_LOADS + B_LOADS + 1;
+    static_assert(C::BM % 64 == 0 && NSA <= C::NLW && (!MX || SB_LOADER < C::NLW), "scale loaders");
+    static_assert(BN * 4 == 64 * 16, "one 16 B-a-lane load covers the column scales");
+    static_assert(NSTAGE * STAGE <= 160 * 1024 && 2 * NLD < 64, "ring");
     __shared__ __align__(16) uint8_t ring[NSTAGE * STAGE];
 
     const int tid = threadIdx.x;
@@ -132,16 +150,26 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const float* __restrict__ ro
         const int lw = wave - C::kCompute;
         const int lrow = lane >> 3;
         const int gchunk = (lane & 7) ^ lrow;
+        // 16 B chunk of the row's 128 K bytes that goes to logical chunk c: c itself,
+        // or in MX mode the MFMA's K order (logical 2q, 2q+1 = K chunks q, 4+q), so
+        // the compute reads pairs (2q, 2q+1) either way
+        auto kchunk = [](int c) { return MX ? ((c >> 1) | ((c & 1) << 2)) : c; };
         int cur = -1;
         uint32_t a_off[A_LOADS];
         const uint8_t* wexp = w;
-        const float* srow = row_scale;
+        const uint32_t* srow = row_scale;
         int ncols = BN;
+        const uint32_t* wsc_mx = w_scale_mx;
         auto setup = [&](int it) __attribute__((always_inline)) {
             const int4 td = tiles[1 + it * G + my];
             const int e = td.x, r0 = td.z, nvalid = td.w & 511;
             const int n0 = td.y * BN;
             ncols = min(BN, N - n0);
+            if (MX) {
+                // lane l: columns 4l .. 4l+3 (past a half tile: the last four again);
+                // N % 128 == 0 and n0 % 256 == 0 keep every address 16 B aligned
+                wsc_mx = w_scale_mx + (int64_t)e * KB * N + n0 + 4 * min(lane, ncols / 4 - 1);
+            }
             int s0 = row_slot[r0];
             if ((uint64_t)s0 >= (uint64_t)T) s0 = 0;
             // all row ids first (one wait), then the selection: rows past the
@@ -154,13 +182,13 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const float* __restrict__ ro
             for (int i = 0; i < A_LOADS; ++i) {
                 const int r = (lw * A_LOADS + i) * 8 + lrow;
                 const int v = (r < nvalid && (uint64_t)sl[i] < (uint64_t)T) ? sl[i] : s0;
-                a_off[i] = (uint32_t)v * (uint32_t)H + (gchunk ^ ((lw * A_LOADS + i) & 1)) * 16;
+                a_off[i] = (uint32_t)v * (uint32_t)H + kchunk(gchunk ^ ((lw * A_LOADS + i) & 1)) * 16;
             }
             wexp = w + ((int64_t)e * N + n0) * H;
             srow = row_scale + r0 + lw * 64;
         };
-        const uint32_t b_lane0 = (uint32_t)lrow * (uint32_t)H + gchunk * 16;
-        const uint32_t b_lane1 = (uint32_t)lrow * (uint32_t)H + (gchunk ^ 1) * 16;
+        const uint32_t b_lane0 = (uint32_t)lrow * (uint32_t)H + kchunk(gchunk) * 16;
+        const uint32_t b_lane1 = (uint32_t)lrow * (uint32_t)H + kchunk(gchunk ^ 1) * 16;
         const uint32_t s_lane = (uint32_t)lane * 4u;
         auto issue = [&](int s) __attribute__((always_inline)) {
             const int it = s / KB, kb = s - it * KB;
@@ -179,16 +207,28 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const float* __restrict__ ro
                     GPTR((wexp + kb * BK + (uint32_t)rb * (uint32_t)H) + (((lw * B_LOADS + i) & 1) ? b_lane1 : b_lane0)),
                     LPTR(base + A_BYTES + (lw * B_LOADS + i) * 1024), 16, 0, 0);
             }
-            __builtin_amdgcn_global_load_lds(GPTR(reinterpret_cast<const uint8_t*>(srow + kb * scale_ld) + s_lane),
-                                             LPTR(base + A_BYTES + B_BYTES + lw * 256), 4, 0, 0);
+            if (lw < NSA)
+                __builtin_amdgcn_global_load_lds(GPTR(reinterpret_cast<const uint8_t*>(srow + kb * scale_ld) + s_lane),
+                                                 LPTR(base + A_BYTES + B_BYTES + lw * 256), 4, 0, 0);
+            else if (MX && lw == SB_LOADER)
+                __builtin_amdgcn_global_load_lds(GPTR(wsc_mx + (int64_t)kb * N),
+                                                 LPTR(base + A_BYTES + B_BYTES + C::NLW * 256), 16, 0, 0);
         };
+        // loads this loader issues per stage (wave-uniform)
+        const bool full = lw < NSA || (MX && lw == SB_LOADER);
         for (int s = 0; s < NSTAGE - 1 && s < nsteps; ++s) issue(s);
         for (int g = 0; g < nsteps; ++g) {
             // stage g has landed once at most the later stages' loads are outstanding
             const int later = min(NSTAGE - 2, nsteps - 1 - g);
-            if (later >= 2) __builtin_amdgcn_s_waitcnt(wait_vm(2 * NLD));
-            else if (later == 1) __builtin_amdgcn_s_waitcnt(wait_vm(NLD));
-            else __builtin_amdgcn_s_waitcnt(wait_vm(0));
+            if (full) {
+                if (later >= 2) __builtin_amdgcn_s_waitcnt(wait_vm(2 * NLD));
+                else if (later == 1) __builtin_amdgcn_s_waitcnt(wait_vm(NLD));
+                else __builtin_amdgcn_s_waitcnt(wait_vm(0));
+            } else {
+                if (later >= 2) __builtin_amdgcn_s_waitcnt(wait_vm(2 * (NLD - 1)));
+                else if (later == 1) __builtin_amdgcn_s_waitcnt(wait_vm(NLD - 1));
+                else __builtin_amdgcn_s_waitcnt(wait_vm(0));
+            }
             cbarrier();
             if (g + NSTAGE - 1 < nsteps) issue(g + NSTAGE - 1);
         }
@@ -219,6 +259,54 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const float* __restrict__ ro
             const uint8_t* As = ring + (g % NSTAGE) * STAGE;
             const uint8_t* Bs = As + A_BYTES;
             const float* Ss = reinterpret_cast<const float*>(Bs + B_BYTES);
+            if constexpr (MX) {
+                // hardware K order of the 16x16x128 fp8 operand: lane quarter q holds
+                // K [16q, 16q+16) and [64+16q, 64+16q+16), K chunks q and 4+q, which the
+                // loaders placed at logical chunks 2q and 2q+1; the scale of (row or
+                // column l & 15, K group l >> 4) comes from lane l
+                const uint32_t* Sa = reinterpret_cast<const uint32_t*>(Bs + B_BYTES);
+                const uint32_t* Sb = Sa + C::NLW * 64;
+                const int qq = lane >> 4;
+                v8i af[MI];
+                int sa[MI];
+#pragma unroll
+                for (int i = 0; i < MI; ++i) {
+                    const int row = wm * RW + i * 16 + (lane & 15);
+                    const int sw_r = (row & 7) ^ ((row >> 3) & 1);
+                    const u32x4 a0 = *reinterpret_cast<const u32x4*>(As + row * BK + (((2 * qq) ^ sw_r) << 4));
+                    const u32x4 a1 = *reinterpret_cast<const u32x4*>(As + row * BK + (((2 * qq + 1) ^ sw_r) << 4));
+                    af[i] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+                    sa[i] = (int)((Sa[row] >> (8 * qq)) & 0xFFu);
+                }
+                auto read_b = [&](int j, uint32_t& sraw) __attribute__((always_inline)) {
+                    const int col = wn * CW + j * 16 + (lane & 15);
+                    const int sw_c = (col & 7) ^ ((col >> 3) & 1);
+                    const u32x4 b0 = *reinterpret_cast<const u32x4*>(Bs + col * BK + (((2 * qq) ^ sw_c) << 4));
+                    const u32x4 b1 = *reinterpret_cast<const u32x4*>(Bs + col * BK + (((2 * qq + 1) ^ sw_c) << 4));
+                    sraw = Sb[col];
+                    return v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+                };
+                uint32_t sbn;
+                v8i bnext = read_b(0, sbn);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const v8i bf = bnext;
+                    // the code is extracted here, after the fence below of the group
+                    // before, so only this group's scale read is waited on
+                    const int sb = (int)((sbn >> (8 * qq)) & 0xFFu);
+                    if (j + 1 < NJ) bnext = read_b(j + 1, sbn);
+                    // keep the next group's reads ahead of this group's MFMAs (left
+                    // alone, the compiler reuses one register set and waits on every read)
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int i = 0; i < MI; ++i)
+                        // transposed sub-tile: weights' fragment and scale first
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            bf, af[i], acc[i][j], 0, 0, 0, sb, 0, sa[i]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                continue;
+            }
             const float sw = wsc[kb];
             v8i af[MI];
             float f[MI];
@@ -311,18 +399,20 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const float* __restrict__ ro
 
 // Pre-pass, one launch:
 //  * row-scale table: out[kb * scale_ld + r] = q_scale[row_slot[r], kb] for the
-//    R expert-major rows (R = expert_offsets[L]).  One thread per row reads its
+//    R expert-major rows (R = expert_offsets[L]), copied as 32-bit words (a
+//    float scale, or four packed e8m0 codes).  One thread per row reads its
 //    slot's contiguous scales; for a fixed kb, consecutive threads write
-//    consecutive floats.  A row id outside [0, T) gets scale 0 (a zero row).
+//    consecutive words.  A row id outside [0, T) gets the word 0 (fp32 scale 0:
+//    a zero row; e8m0 codes 0: the scale 2^-127 on slot 0's payload).
 //  * tile descriptors (the last workgroup): per local expert ceil(count / BM)
 //    row tiles times NT column tiles, experts in order, column tiles outer and
 //    row tiles inner; tiles[0].x = number of tiles, tiles[1 + t] =
 //    {expert, column tile, first row, valid rows | row tile << 9}.
 template <int BM>
 __global__ void __launch_bounds__(256)
-gemm1_prep_kernel(const float* __restrict__ q_scale, const int32_t* __restrict__ row_slot,
+gemm1_prep_kernel(const uint32_t* __restrict__ q_scale, const int32_t* __restrict__ row_slot,
                   const int32_t* __restrict__ expert_offsets, int L, int KB, int NT, int64_t T,
-                  int64_t rows_cap, int64_t scale_ld, float* __restrict__ out, int4* __restrict__ tiles,
+                  int64_t rows_cap, int64_t scale_ld, uint32_t* __restrict__ out, int4* __restrict__ tiles,
                   int64_t tiles_cap) {
     if (blockIdx.x == gridDim.x - 1) {
         __shared__ int eoff[kMaxL + 1];
@@ -389,11 +479,11 @@ gemm1_prep_kernel(const float* __restrict__ q_scale, const int32_t* __restrict__
         const int64_t r = item - (int64_t)kg * R;
         const int s = row_slot[r];
         const bool ok = (uint64_t)s < (uint64_t)T;
-        const float* src = q_scale + (int64_t)(ok ? s : 0) * KB;
+        const uint32_t* src = q_scale + (int64_t)(ok ? s : 0) * KB;
         const int k0 = kg * kPrepKb;
-        float v[kPrepKb];
+        uint32_t v[kPrepKb];
 #pragma unroll
-        for (int i = 0; i < kPrepKb; ++i) v[i] = (ok && k0 + i < KB) ? src[k0 + i] : 0.0f;
+        for (int i = 0; i < kPrepKb; ++i) v[i] = (ok && k0 + i < KB) ? src[k0 + i] : 0u;
 #pragma unroll
         for (int i = 0; i < kPrepKb; ++i)
             if (k0 + i < KB) out[(int64_t)(k0 + i) * scale_ld + r] = v[i];
@@ -443,12 +533,14 @@ extern "C" moe_status moe_grouped_gemm1_workspace(const moe_dims* dims, int32_t 
     return MOE_OK;
 }
 
-extern "C" moe_status moe_grouped_gemm1(const moe_dims* dims, int32_t n, const uint8_t* q_e4m3,
-                                        const float* q_scale, const int32_t* row_slot,
-                                        const int32_t* expert_offsets, const int32_t* totals,
-                                        const uint8_t* w_e4m3, const float* w_scale, uint16_t* y_bf16,
-                                        void* ws, size_t ws_bytes, void* hip_stream) {
-    (void)totals;
+namespace {
+
+// One GEMM1 call: the pre-pass (row-scale table and tile descriptors) and the
+// main kernel; q_scale and w_scale are fp32 scales or packed e8m0 codes (MX).
+template <bool MX>
+moe_status run_gemm1(const moe_dims* dims, int32_t n, const uint8_t* q_e4m3, const uint32_t* q_scale,
+                     const int32_t* row_slot, const int32_t* expert_offsets, const uint8_t* w_e4m3,
+                     const void* w_scale, uint16_t* y_bf16, void* ws, size_t ws_bytes, void* hip_stream) {
     moe::Dims d;
     moe_status st = moe::load_dims(dims, &d, true);
     if (st != MOE_OK) return st;
@@ -471,7 +563,7 @@ extern "C" moe_status moe_grouped_gemm1(const moe_dims* dims, int32_t n, const u
     int cus = cu_count();
     if (cus <= 0) return MOE_ERR_HIP;
     hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
-    float* row_scale = reinterpret_cast<float*>(ws);
+    uint32_t* row_scale = reinterpret_cast<uint32_t*>(ws);
     int4* tiles = reinterpret_cast<int4*>(static_cast<uint8_t*>(ws) + wl.table_bytes);
     const int NT = (int)((n + BN - 1) / BN);
     // gather workgroups plus the planning workgroup (the last one)
@@ -482,8 +574,29 @@ extern "C" moe_status moe_grouped_gemm1(const moe_dims* dims, int32_t n, const u
                        wl.tiles_cap);
     if ((st = moe::launch_status()) != MOE_OK) return st;
     const int grid = ((cus + kXcds - 1) / kXcds) * kXcds;
-    hipLaunchKernelGGL((grouped_gemm1_kernel<TileCfg>), dim3(grid), dim3(TileCfg::kThreads), 0, stream,
+    hipLaunchKernelGGL((grouped_gemm1_kernel<TileCfg, MX>), dim3(grid), dim3(TileCfg::kThreads), 0, stream,
                        q_e4m3, row_scale, tiles, row_slot, w_e4m3, w_scale, y_bf16, (int)n, (int)d.H, d.T,
                        wl.scale_ld);
     return moe::launch_status();
+}
+
+}  // namespace
+
+extern "C" moe_status moe_grouped_gemm1(const moe_dims* dims, int32_t n, const uint8_t* q_e4m3,
+                                        const float* q_scale, const int32_t* row_slot,
+                                        const int32_t* expert_offsets, const int32_t* totals,
+                                        const uint8_t* w_e4m3, const float* w_scale, uint16_t* y_bf16,
+                                        void* ws, size_t ws_bytes, void* hip_stream) {
+    (void)totals;
+    return run_gemm1<false>(dims, n, q_e4m3, reinterpret_cast<const uint32_t*>(q_scale), row_slot,
+                            expert_offsets, w_e4m3, w_scale, y_bf16, ws, ws_bytes, hip_stream);
+}
+
+extern "C" moe_status moe_grouped_gemm1_mx(const moe_dims* dims, int32_t n, const uint8_t* q_e4m3,
+                                           const uint32_t* q_scale, const int32_t* row_slot,
+                                           const int32_t* expert_offsets, const uint8_t* w_e4m3,
+                                           const uint32_t* w_scale, uint16_t* y_bf16, void* ws,
+                                           size_t ws_bytes, void* hip_stream) {
+    return run_gemm1<true>(dims, n, q_e4m3, q_scale, row_slot, expert_offsets, w_e4m3, w_scale, y_bf16, ws,
+                           ws_bytes, hip_stream);
 }

@@ -149,6 +149,94 @@ quant_dispatch_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict_
     }
 }
 
+// MX-style variant ("Where we stand": e8m0 block scales; commit
+// "ready-first / quant-lds-store": packed four per dword): groups of 32
+// elements, a group being one lane pair of the mapping above.  Per group:
+// t = amax / 448 (IEEE fp32), E = ceil(log2 t) read off t's bits (an exact
+// power of two keeps its exponent, anything above it rounds up), clamped to
+// [-127, 127] (an all-zero group: -127); payload = e4m3(x * 2^-E), the scaling
+// exact, so the hardware conversion's round to nearest even is the only
+// rounding and no magnitude exceeds 448 (an all-zero group: zero bytes);
+// code = E + 127, the four codes of a 128-element block packed into one dword
+// (group g of the block in byte g).
+__device__ __forceinline__ int ceil_log2_over_448(uint32_t amax_bits16) {
+    if (amax_bits16 == 0) return -127;
+    const float t = __uint_as_float(amax_bits16 << 16) / 448.0f;
+    const uint32_t b = __float_as_uint(t);
+    const int ex = (int)((b >> 23) & 0xFF);
+    const uint32_t man = b & 0x7FFFFFu;
+    int E;
+    if (ex == 0) E = man > 0x400000u ? -126 : -127;     // subnormal t: (2^-127, 2^-126) or below
+    else E = ex - 127 + (man != 0 ? 1 : 0);
+    return max(-127, min(127, E));
+}
+
+__global__ void __launch_bounds__(kBlock)
+quant_dispatch_mx_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ slot_tok,
+                         const int32_t* __restrict__ totals, int64_t T, int H,
+                         uint8_t* __restrict__ q, uint32_t* __restrict__ q_scale) {
+    const int64_t U = min((int64_t)totals[1], T);
+    const int lane = threadIdx.x % MOE_WAVE;
+    const int sub = lane & 7;
+    const int nblk = H / 128;
+    const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+    const int per = ((nblk + 8 * kSplit - 1) / (8 * kSplit)) * 8;
+    for (int64_t it = (int64_t)blockIdx.x * kWaves + threadIdx.x / MOE_WAVE; it < U * kSplit; it += nwaves) {
+        const int64_t u = it / kSplit;
+        const int b0 = (int)(it - u * kSplit) * per;
+        const int b1 = min(nblk, b0 + per);
+        if (b0 >= b1) continue;
+        const int g = slot_tok[u];
+        if ((uint64_t)g >= (uint64_t)T) continue;
+        const moe::u32x4* src = reinterpret_cast<const moe::u32x4*>(x + (int64_t)g * H);
+        moe::u32x4* dst = reinterpret_cast<moe::u32x4*>(q + u * H);
+        uint32_t* sdst = q_scale + u * nblk;
+        auto load = [&](int cb, moe::u32x4& a, moe::u32x4& b) __attribute__((always_inline)) {
+            const int blk = min(cb + (lane >> 3), b1 - 1);
+            a = src[blk * 16 + sub * 2];
+            b = src[blk * 16 + sub * 2 + 1];
+        };
+        moe::u32x4 n0, n1;
+        load(b0, n0, n1);
+        for (int cb = b0; cb < b1; cb += 8) {
+            const int blk = cb + (lane >> 3);
+            const bool act = blk < b1;
+            const moe::u32x4 v0 = n0, v1 = n1;
+            if (cb + 8 < b1) load(cb + 8, n0, n1);
+            const uint32_t wv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            u16x2 m2 = {0, 0};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t a = wv[i] & 0x7FFF7FFFu;
+                m2 = __builtin_elementwise_max(m2, *reinterpret_cast<const u16x2*>(&a));
+            }
+            uint32_t m = max((uint32_t)m2.x, (uint32_t)m2.y);
+            m = max(m, dpp<0xB1>(m));                     // the lane pair = one group of 32
+            const int E = ceil_log2_over_448(m);
+            const float p2 = __uint_as_float((uint32_t)(127 - E) << 23);   // 2^-E, E <= 120 for bf16
+            // an all-zero group (negative zeros included) stores zero bytes
+            const bool zero = m == 0;
+            uint32_t out[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                out[i] = zero ? 0u
+                              : cvt4(moe::bf16_lo(wv[2 * i]) * p2, moe::bf16_hi(wv[2 * i]) * p2,
+                                     moe::bf16_lo(wv[2 * i + 1]) * p2, moe::bf16_hi(wv[2 * i + 1]) * p2);
+            // codes of the block's groups 0..3 sit in lanes sub = 0, 2, 4, 6
+            const uint32_t code = (uint32_t)(E + 127);
+            const int base = lane & ~7;
+            const uint32_t packed = (uint32_t)__shfl((int)code, base, MOE_WAVE) |
+                                    ((uint32_t)__shfl((int)code, base + 2, MOE_WAVE) << 8) |
+                                    ((uint32_t)__shfl((int)code, base + 4, MOE_WAVE) << 16) |
+                                    ((uint32_t)__shfl((int)code, base + 6, MOE_WAVE) << 24);
+            if (act) {
+                __builtin_nontemporal_store(moe::u32x4{out[0], out[1], out[2], out[3]}, dst + blk * 8 + sub);
+                if (sub == 0) sdst[blk] = packed;
+            }
+        }
+    }
+}
+
 }  // namespace
 
 extern "C" moe_status moe_quant_dispatch(const moe_dims* dims, const uint16_t* x_bf16,
@@ -163,6 +251,23 @@ extern "C" moe_status moe_quant_dispatch(const moe_dims* dims, const uint16_t* x
     const int64_t waves = d.T * kSplit;                          // one per row piece (slots_cap = T)
     const int grid = (int)std::min<int64_t>((waves + kWaves - 1) / kWaves, 16384);
     hipLaunchKernelGGL(quant_dispatch_kernel, dim3(grid), dim3(kBlock), 0,
+                       reinterpret_cast<hipStream_t>(hip_stream), x_bf16, slot_tok, totals, d.T,
+                       (int)d.H, q_e4m3, q_scale);
+    return moe::launch_status();
+}
+
+extern "C" moe_status moe_quant_dispatch_mx(const moe_dims* dims, const uint16_t* x_bf16,
+                                            const int32_t* slot_tok, const int32_t* totals,
+                                            uint8_t* q_e4m3, uint32_t* q_scale, void* hip_stream) {
+    moe::Dims d;
+    moe_status st = moe::load_dims(dims, &d, true);
+    if (st != MOE_OK) return st;
+    if (d.T == 0) return MOE_OK;
+    if (!x_bf16 || !slot_tok || !totals || !q_e4m3 || !q_scale) return MOE_ERR_INVALID_ARG;
+    if (d.T * d.H >= ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
+    const int64_t waves = d.T * kSplit;
+    const int grid = (int)std::min<int64_t>((waves + kWaves - 1) / kWaves, 16384);
+    hipLaunchKernelGGL(quant_dispatch_mx_kernel, dim3(grid), dim3(kBlock), 0,
                        reinterpret_cast<hipStream_t>(hip_stream), x_bf16, slot_tok, totals, d.T,
                        (int)d.H, q_e4m3, q_scale);
     return moe::launch_status();

@@ -167,6 +167,54 @@ moe_status moe_grouped_gemm1(const moe_dims* dims, int32_t n,
                              uint16_t* y_bf16, void* ws, size_t ws_bytes, void* hip_stream);
 
 /*
+ * MX-style variants of steps 2 and 3: fp8 e4m3 payloads with power-of-two
+ * (e8m0) scales per 32 consecutive hidden elements, the scales applied by the
+ * matrix cores' block-scale operands ("poc(cco): MegaMoE stage1 dispatch over
+ * SDMA", "Where we stand": the stage1 runs use e8m0 block scales; commit
+ * "ready-first / quant-lds-store": four e8m0 codes packed per dword).  The
+ * pages fix neither the scale rule nor the packing order; the reading taken:
+ *
+ * For slot u < U, token g = slot_tok[u], group j < H/32 (elements 32j .. 32j+31):
+ *   a = max |x[g, group j]|;  a == 0: E = -127 and zero bytes;
+ *   else t = a / 448 (IEEE fp32), E = ceil(log2 t) exactly (an exact power of
+ *   two keeps its exponent), clamped to [-127, 127];
+ *   q[u, 32j+i] = e4m3(x[g, 32j+i] * 2^-E)  (the scaling is exact; round to
+ *   nearest even; never above 448 in magnitude; sign kept on zero);
+ *   code = E + 127 (e8m0: value 2^(code-127));
+ *   q_scale[u, b] = codes of groups 4b, 4b+1, 4b+2, 4b+3 in bytes 0, 1, 2, 3.
+ * In:  as moe_quant_dispatch.
+ * Out: q_e4m3 uint8 [slots_cap, H];  q_scale uint32 [slots_cap, H/128].
+ * Rows past U are not written.
+ */
+moe_status moe_quant_dispatch_mx(const moe_dims* dims, const uint16_t* x_bf16,
+                                 const int32_t* slot_tok, const int32_t* totals,
+                                 uint8_t* q_e4m3, uint32_t* q_scale, void* hip_stream);
+
+/*
+ * MX GEMM1: as moe_grouped_gemm1 with both operands' scales per 32-element K
+ * group: for local expert le, row r of it, column c < n,
+ *   y[r, c] = bf16( sum_h  q[row_slot[r], h] * 2^(Ea(row_slot[r], h/32))
+ *                        * w[le, c, h]    * 2^(Eb(le, c, h/32)) )
+ * accumulated in fp32 by the fp8 MFMA with its e8m0 block-scale operands.
+ * In:  q_e4m3, q_scale (uint32 [slots_cap, H/128]) from moe_quant_dispatch_mx;
+ *      row_slot, expert_offsets from step 1 (read on the device);
+ *      w_e4m3  uint8 [L, n, H] (as moe_grouped_gemm1);
+ *      w_scale uint32 [L, H/128, n]: the packed codes of column c's groups
+ *              4kb .. 4kb+3 at [le, kb, c] (K-block-major, so one K block's
+ *              scales for consecutive columns are contiguous).
+ * Out: y_bf16 uint16 (bf16 bits) [rows_cap, n]; rows past R are not written.
+ * ws: the workspace moe_grouped_gemm1_workspace sizes for (dims, n).
+ * n must be a positive multiple of 128.  A row id outside [0, T) (which step 1
+ * cannot produce) reads slot 0's payload with the scale 2^-127: no access
+ * leaves the buffers, and that row's values are not specified.
+ */
+moe_status moe_grouped_gemm1_mx(const moe_dims* dims, int32_t n,
+                                const uint8_t* q_e4m3, const uint32_t* q_scale,
+                                const int32_t* row_slot, const int32_t* expert_offsets,
+                                const uint8_t* w_e4m3, const uint32_t* w_scale,
+                                uint16_t* y_bf16, void* ws, size_t ws_bytes, void* hip_stream);
+
+/*
  * Step 4: combine.  Top-k weighted gather-sum back to token order (TilePipe:
  * push combine to the token owners; "MegaMoE stage1 dispatch over SDMA",
  * "What": stage2 + combine).
