@@ -10,7 +10,12 @@ on (torch's current stream, which the binding passes to the library).
 Prints ONE JSON line.  `value` is stage1 = layout + quant + GEMM1 in
 microseconds per step (lower is better); the line also carries the dispatch /
 combine HBM GB/s, the GEMM1 fp8 TFLOP/s, a roofline entry per kernel and the
-CPU oracle timed on a bounded sample of the same workload.
+CPU oracle timed on a bounded sample of the same workload.  After the timed
+steps, the MX-style variant of stage1 (e8m0 scales per 32 K elements: layout
+-> moe_quant_dispatch_mx -> moe_grouped_gemm1_mx) is timed on the same inputs
+in a separate A/B loop that alternates one fp32-scale stage1 step with one MX
+step (the clock drifts over a run, so only interleaved numbers compare), and
+reported under "mx".
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--no-cpu-baseline] [--copy-calib]
@@ -79,9 +84,12 @@ def algorithmic(w, R, U, Rc):
     quant = U * 4 + U * H * 2 + U * H + U * (H // 128) * 4
     gemm_flop = 2 * R * H * N
     gemm_bytes = U * (H + H // 32) + L * N * H + L * N * H // (128 * 128) * 4 + R * N * 2
+    # MX: the same payloads; one packed dword of e8m0 codes per 128 K elements on
+    # both operands (activations: as the fp32 scale; weights: per column)
+    gemm_mx_bytes = U * (H + H // 32) + L * N * H + L * N * (H // 128) * 4 + R * N * 2
     combine = Rc * width * 2 + T * k * 8 + T * width * 2
     return dict(layout_local=lay_local, quant=quant, gemm1_flop=gemm_flop, gemm1_bytes=gemm_bytes,
-                layout_full=lay_full, combine=combine)
+                layout_full=lay_full, combine=combine, quant_mx=quant, gemm1_mx_bytes=gemm_mx_bytes)
 
 
 def main():
@@ -199,6 +207,9 @@ def main():
     # stage1 (layout -> quant -> GEMM1) captured once in a graph and replayed; the
     # calls read their counts on the device, so the capture needs no host sync
     graph = stage1_graph(torch, moe, d_loc, ids_d, x_d, wq_d, ws_d, lay, q, qs, y1, g_ws, w, R, U, args.steps)
+    mx = mx_stage1(torch, moe, w, d_loc, ids_d, x_d, lay, g_ws, alg, traffic, args,
+                   fp32_step=lambda: (moe.quant_dispatch(d_loc, x_d, lay, q, qs),
+                                      moe.grouped_gemm1(d_loc, w.N, q, qs, lay, wq_d, ws_d, y1, g_ws)))
     ceil = ceilings(torch, moe, args.copy_calib)
 
     rec = {
@@ -217,6 +228,7 @@ def main():
         "roofline": roof,
         "percentiles_us": spread,
         "stage1_graph": graph,
+        "mx": mx,
         "ceilings": ceil,
         "fraction_of_measured_ceilings": {
             "gemm1_vs_mfma_loop": round(gemm_tflops / ceil["mfma_fp8_tflops"], 4),
@@ -227,6 +239,70 @@ def main():
         rec["cpu_baseline"] = cpu_baseline(w, ids, wts, lay, lay_all, q, qs, y1, out, Y_d, R, U, stage1)
 
     print(json.dumps(rec), flush=True)
+
+
+def mx_stage1(torch, moe, w, d, ids_d, x_d, lay, g_ws, alg, traffic, args, fp32_step):
+    """The MX-style stage1 (layout -> quant_mx -> GEMM1 MX) on the same inputs:
+    `warmup` untimed, then `steps` A/B pairs, each an fp32-scale stage1 step
+    followed by an MX step, HIP events between the calls."""
+    import workloads
+    t0 = time.time()
+    wq, ws = workloads.weights_mx(w)
+    log(f"[bench] MX weights generated in {time.time() - t0:.1f}s")
+    wq_d = torch.from_numpy(wq).cuda()
+    ws_d = torch.from_numpy(ws.view(np.int32)).cuda()
+    del wq, ws
+    q = torch.empty((w.T, w.H), dtype=torch.uint8, device="cuda")
+    qs = torch.empty((w.T, w.H // 128), dtype=torch.int32, device="cuda")
+    y = torch.empty((w.T * w.k, w.N), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    names = ["layout_local", "quant_mx", "gemm1_mx"]
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        moe.route_layout(d, ids_d, lay)
+        if ev: ev[1].record(stream)
+        moe.quant_dispatch_mx(d, x_d, lay, q, qs)
+        if ev: ev[2].record(stream)
+        moe.grouped_gemm1_mx(d, w.N, q, qs, lay, wq_d, ws_d, y, g_ws)
+        if ev: ev[3].record(stream)
+
+    def step_fp32(ev):
+        ev[0].record(stream)
+        moe.route_layout(d, ids_d, lay)
+        fp32_step()
+        ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step_fp32(evf[i])
+        step(evs[i])
+    torch.cuda.synchronize()
+    per = {n: [e[j].elapsed_time(e[j + 1]) * 1e3 for e in evs] for j, n in enumerate(names)}
+    med = {n: float(np.median(v)) for n, v in per.items()}
+    stage1 = [sum(per[n][i] for n in names) for i in range(args.steps)]
+    stage1_fp32 = [e[0].elapsed_time(e[1]) * 1e3 for e in evf]
+    qa = alg["quant_mx"] / (med["quant_mx"] * 1e-6) / 1e9
+    ga = alg["gemm1_flop"] / (med["gemm1_mx"] * 1e-6) / 1e12
+    del wq_d, ws_d, q, qs, y
+    return {"stage1_us": round(float(np.median(stage1)), 2),
+            "stage1_p10_p90_us": [round(float(np.percentile(stage1, 10)), 2),
+                                  round(float(np.percentile(stage1, 90)), 2)],
+            "fp32_scale_stage1_us_same_loop": round(float(np.median(stage1_fp32)), 2),
+            "mx_over_fp32_stage1": round(float(np.median(stage1)) / float(np.median(stage1_fp32)), 4),
+            "kernels_us_median": {n: round(med[n], 2) for n in names},
+            "kernels": {
+                "quant_mx": {"bound": "hbm", "achieved": round(qa, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(qa / HBM_PEAK_GBS, 4), "traffic": traffic.get("quant_mx"),
+                             "algorithmic_bytes": int(alg["quant_mx"])},
+                "gemm1_mx": {"bound": "mfma", "achieved": round(ga, 1), "peak": FP8_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(ga / FP8_PEAK_TFLOPS, 4),
+                             "traffic": traffic.get("gemm1_mx"), "algorithmic_flop": int(alg["gemm1_flop"]),
+                             "algorithmic_bytes": int(alg["gemm1_mx_bytes"])}}}
 
 
 def stage1_graph(torch, moe, d, ids_d, x_d, wq_d, ws_d, lay, q, qs, y1, g_ws, w, R, U, steps):
