@@ -24,6 +24,11 @@ Each function is the plain definition of one step, written from the pages:
   the pages' own scale format: power-of-two (e8m0) scales per group of 32 K
   elements, packed four per dword (MegaMoE PR, "Where we stand" and commit
   "ready-first / quant-lds-store").
+* ``stage2.act_quant`` / ``stage2.grouped_gemm2`` / ``stage2.combine_rows`` -
+  stage2 after GEMM1: silu(gate) * up, its fp8 quantisation, the grouped
+  down-projection with each row's routing weight, and the combine of the
+  weighted rows (MegaMoE PR, "What": stage1 feeds stage2 + combine; commit
+  "recv_layout": the layout's per-row routing weights serve stage2).
 * ``fp8`` / ``bf16`` - the OCP FP8 E4M3 encoding and bf16 rounding the steps
   rely on.
 
@@ -32,4 +37,4 @@ invariants (bijection, contiguity, stability, half-ulp round trip, identity
 experts), torch's independent fp8/bf16 casts, and exact special cases.
 Every function here has at least one such pin; none is "parity unpinned".
 """
-from . import bf16, fp8, layout, quant, gemm1, combine  # noqa: F401
+from . import bf16, fp8, layout, quant, gemm1, combine, mx, stage2  # noqa: F401

@@ -28,7 +28,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "get", "routing", "activations", "weights",
-    "expert_outputs", "sha256",
+    "expert_outputs", "weights2", "stage2_inputs", "sha256",
 ]
 
 
@@ -84,7 +84,8 @@ def get(name: str) -> Workload:
 
 # ----------------------------------------------------------------------------
 # seeding
-_STREAMS = ("routing", "activations", "weights", "expert_outputs")
+# appending a stream keeps the earlier streams' draws (SeedSequence children by index)
+_STREAMS = ("routing", "activations", "weights", "expert_outputs", "weights2", "stage2_inputs")
 _CHUNK_ROWS = 1024
 
 
@@ -157,37 +158,53 @@ def activations(w: Workload) -> np.ndarray:
 
 
 def weights(w: Workload, experts: range | None = None):
-    """GEMM1 weights for the local experts.
+    """GEMM1 weights for the local experts (see ``_block_fp8_weights``).
 
     Logical weight of local expert le is [H, N] (K x N); it is stored
-    K-contiguous as [N, H] bytes.  Recipe: fp32 N(0, 0.02) -> bf16 (RNE) -> one
-    fp32 scale per 128(N) x 128(K) block = block |max| / 448 -> e4m3 bytes of
-    value / scale (torch's float8_e4m3fn cast; every quotient is <= 448 in
-    magnitude, so the cast never overflows).  An all-zero block gets scale 0
-    and zero bytes.
+    K-contiguous as [N, H] bytes.
 
     Returns (w_e4m3 uint8 [L', N, H], w_scale float32 [L', N/128, H/128]).
     """
+    return _block_fp8_weights(_stream(w.seed, "weights"), w.L, w.N, w.H, experts)
+
+
+def weights2(w: Workload, experts: range | None = None):
+    """GEMM2 (down projection) weights for the local experts: logical [I, H]
+    (K = I = N/2 rows of GEMM1's output width, H output columns), stored
+    K-contiguous as [H, I] bytes, same recipe as ``weights``.
+
+    Returns (w2_e4m3 uint8 [L', H, I], w2_scale float32 [L', H/128, I/128]).
+    """
+    assert w.N % 256 == 0, "GEMM1 width must be 2*I with I a multiple of 128"
+    return _block_fp8_weights(_stream(w.seed, "weights2"), w.L, w.H, w.N // 2, experts)
+
+
+def _block_fp8_weights(ss: np.random.SeedSequence, L: int, N: int, K: int, experts):
+    """[L', N, K] e4m3 bytes + [L', N/128, K/128] fp32 scales, expert le drawn from
+    its own spawned seed.  Recipe: fp32 N(0, 0.02) -> bf16 (RNE) -> one fp32
+    scale per 128(N) x 128(K) block = block |max| / 448 -> e4m3 bytes of
+    value / scale (torch's float8_e4m3fn cast; every quotient is <= 448 in
+    magnitude, so the cast never overflows).  An all-zero block gets scale 0
+    and zero bytes."""
     import torch
-    L, N, H = w.L, w.N, w.H
     experts = range(L) if experts is None else experts
-    seeds = _stream(w.seed, "weights").spawn(L)
-    q = np.empty((len(experts), N, H), dtype=np.uint8)
-    sc = np.empty((len(experts), N // 128, H // 128), dtype=np.float32)
+    seeds = ss.spawn(L)
+    q = np.empty((len(experts), N, K), dtype=np.uint8)
+    sc = np.empty((len(experts), N // 128, K // 128), dtype=np.float32)
 
     def one(i_le):
         i, le = i_le
         g = np.random.default_rng(seeds[le])
-        wf = g.standard_normal(size=(N, H), dtype=np.float32)
+        wf = g.standard_normal(size=(N, K), dtype=np.float32)
         wf *= np.float32(0.02)
         t = torch.from_numpy(wf).to(torch.bfloat16).to(torch.float32)
-        blk = t.view(N // 128, 128, H // 128, 128)
-        amax = blk.abs().amax(dim=(1, 3))                       # [N/128, H/128]
+        blk = t.view(N // 128, 128, K // 128, 128)
+        amax = blk.abs().amax(dim=(1, 3))                       # [N/128, K/128]
         s = amax / torch.tensor(448.0, dtype=torch.float32)
         safe = torch.where(s > 0, s, torch.ones_like(s))
         v = blk / safe[:, None, :, None]
         v = torch.where((s > 0)[:, None, :, None], v, torch.zeros_like(v))
-        q[i] = v.to(torch.float8_e4m3fn).view(torch.uint8).reshape(N, H).numpy()
+        q[i] = v.to(torch.float8_e4m3fn).view(torch.uint8).reshape(N, K).numpy()
         sc[i] = s.numpy()
 
     items = list(enumerate(experts))
@@ -198,6 +215,14 @@ def weights(w: Workload, experts: range | None = None):
         with _cf.ThreadPoolExecutor(min(_threads(), 8)) as ex:
             list(ex.map(one, items))
     return q, sc
+
+
+def stage2_inputs(w: Workload, rows: int | None = None) -> np.ndarray:
+    """Synthetic GEMM1 outputs for testing stage2 apart from GEMM1: bf16
+    N(0, 1.7) [rows, N] (default rows = T*k; 1.7 ~ the spread of GEMM1's
+    outputs, sqrt(H) * 0.02 at H = 7168) as uint16 bits."""
+    rows = w.T * w.k if rows is None else rows
+    return _to_bf16_bits(_chunked_normal(_stream(w.seed, "stage2_inputs"), rows, w.N, 1.7))
 
 
 def expert_outputs(w: Workload, rows: int | None = None, width: int | None = None) -> np.ndarray:
