@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_hotpath.so")
-SOURCES = ["api.hip", "layout.hip", "quant.hip", "gemm1.hip", "combine.hip"]
+SOURCES = ["api.hip", "layout.hip", "quant.hip", "gemm1.hip", "stage2.hip", "combine.hip"]
 CEILING_LIB = os.path.join(PKG, "libmoe_ceiling.so")
 CEILING_SOURCES = ["ceiling.hip"]
 ARCH = "gfx950"

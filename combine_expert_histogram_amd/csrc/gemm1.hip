@@ -108,7 +108,10 @@ struct Cfg {
 // rows' dwords gathered into the row-scale table, the weights' dwords stored
 // [L, H/128, N]); they ride in the MFMA's block-scale operands, so the K blocks
 // accumulate in the MFMA itself and there is no fold.
-template <class C, bool MX>
+// DIRECT: the A operand's rows are the expert-major rows themselves (row r of
+// the tile reads A row r; GEMM2 on stage2's output), instead of rows gathered
+// through the rowmap; T is then the number of A rows.
+template <class C, bool MX, bool DIRECT>
 __global__ void __launch_bounds__(C::kThreads, 1)
 grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__ row_scale,
                      const int4* __restrict__ tiles, const int32_t* __restrict__ row_slot,
@@ -170,14 +173,15 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
                 // N % 128 == 0 and n0 % 256 == 0 keep every address 16 B aligned
                 wsc_mx = w_scale_mx + (int64_t)e * KB * N + n0 + 4 * min(lane, ncols / 4 - 1);
             }
-            int s0 = row_slot[r0];
+            int s0 = DIRECT ? r0 : row_slot[r0];
             if ((uint64_t)s0 >= (uint64_t)T) s0 = 0;
             // all row ids first (one wait), then the selection: rows past the
             // expert's last row reuse the first row's slot
             int sl[A_LOADS];
 #pragma unroll
             for (int i = 0; i < A_LOADS; ++i)
-                sl[i] = row_slot[r0 + min((lw * A_LOADS + i) * 8 + lrow, nvalid - 1)];
+                sl[i] = DIRECT ? r0 + min((lw * A_LOADS + i) * 8 + lrow, nvalid - 1)
+                               : row_slot[r0 + min((lw * A_LOADS + i) * 8 + lrow, nvalid - 1)];
 #pragma unroll
             for (int i = 0; i < A_LOADS; ++i) {
                 const int r = (lw * A_LOADS + i) * 8 + lrow;
@@ -400,10 +404,14 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
 // Pre-pass, one launch:
 //  * row-scale table: out[kb * scale_ld + r] = q_scale[row_slot[r], kb] for the
 //    R expert-major rows (R = expert_offsets[L]), copied as 32-bit words (a
-//    float scale, or four packed e8m0 codes).  One thread per row reads its
-//    slot's contiguous scales; for a fixed kb, consecutive threads write
-//    consecutive words.  A row id outside [0, T) gets the word 0 (fp32 scale 0:
-//    a zero row; e8m0 codes 0: the scale 2^-127 on slot 0's payload).
+//    float scale, or four packed e8m0 codes); with no rowmap (row_slot null)
+//    row r's own scales.  With row weights (row_assign and topk_w non-null,
+//    fp32 scales only) each scale is multiplied by the row's routing weight
+//    topk_w[row_assign[r]], which so scales the row's whole output.  One
+//    thread per row reads its slot's contiguous scales; for a fixed kb,
+//    consecutive threads write consecutive words.  A row id outside [0, T)
+//    gets the word 0 (fp32 scale 0: a zero row; e8m0 codes 0: the scale
+//    2^-127 on slot 0's payload), as does a weight index outside [0, n_assign).
 //  * tile descriptors (the last workgroup): per local expert ceil(count / BM)
 //    row tiles times NT column tiles, experts in order, column tiles outer and
 //    row tiles inner; tiles[0].x = number of tiles, tiles[1 + t] =
@@ -411,6 +419,7 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
 template <int BM>
 __global__ void __launch_bounds__(256)
 gemm1_prep_kernel(const uint32_t* __restrict__ q_scale, const int32_t* __restrict__ row_slot,
+                  const int32_t* __restrict__ row_assign, const float* __restrict__ topk_w, int64_t n_assign,
                   const int32_t* __restrict__ expert_offsets, int L, int KB, int NT, int64_t T,
                   int64_t rows_cap, int64_t scale_ld, uint32_t* __restrict__ out, int4* __restrict__ tiles,
                   int64_t tiles_cap) {
@@ -477,13 +486,23 @@ gemm1_prep_kernel(const uint32_t* __restrict__ q_scale, const int32_t* __restric
     for (int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x; item < R * KG; item += nthr) {
         const int kg = (int)(item / R);
         const int64_t r = item - (int64_t)kg * R;
-        const int s = row_slot[r];
-        const bool ok = (uint64_t)s < (uint64_t)T;
+        const int s = row_slot ? row_slot[r] : (int)r;
+        bool ok = (uint64_t)s < (uint64_t)T;
+        float wr = 1.0f;
+        if (topk_w) {
+            const int ra = row_assign[r];
+            ok = ok && (uint64_t)ra < (uint64_t)n_assign;
+            wr = ok ? topk_w[ra] : 0.0f;
+        }
         const uint32_t* src = q_scale + (int64_t)(ok ? s : 0) * KB;
         const int k0 = kg * kPrepKb;
         uint32_t v[kPrepKb];
 #pragma unroll
         for (int i = 0; i < kPrepKb; ++i) v[i] = (ok && k0 + i < KB) ? src[k0 + i] : 0u;
+        if (topk_w) {
+#pragma unroll
+            for (int i = 0; i < kPrepKb; ++i) v[i] = __float_as_uint(__uint_as_float(v[i]) * wr);
+        }
 #pragma unroll
         for (int i = 0; i < kPrepKb; ++i)
             if (k0 + i < KB) out[(int64_t)(k0 + i) * scale_ld + r] = v[i];
@@ -512,51 +531,41 @@ static_assert(TileCfg::BM <= kMaxBM, "scale table padding covers one tile");
 struct WsLayout {
     int64_t scale_ld, table_bytes, tiles_cap, bytes;
 };
-WsLayout ws_layout(const moe::Dims& d, int n) {
+// rows_cap expert-major rows, KB K blocks, n output columns, L experts
+WsLayout ws_layout(int64_t rows_cap, int64_t KB, int64_t n, int64_t L) {
     WsLayout l;
-    const int64_t rows_cap = d.T * d.k;
     l.scale_ld = scale_ld_of(rows_cap);
-    l.table_bytes = ((d.H / BK) * l.scale_ld * 4 + 255) & ~int64_t(255);
-    l.tiles_cap = (rows_cap / kMinBM + d.L) * ((n + BN - 1) / BN);
+    l.table_bytes = (KB * l.scale_ld * 4 + 255) & ~int64_t(255);
+    l.tiles_cap = (rows_cap / kMinBM + L) * ((n + BN - 1) / BN);
     l.bytes = l.table_bytes + (1 + l.tiles_cap) * 16;
     return l;
 }
 
-}  // namespace
-
-extern "C" moe_status moe_grouped_gemm1_workspace(const moe_dims* dims, int32_t n, size_t* bytes) {
-    moe::Dims d;
-    moe_status st = moe::load_dims(dims, &d, true);
-    if (st != MOE_OK) return st;
-    if (!bytes || n < 128 || n % 128 != 0) return MOE_ERR_INVALID_ARG;
-    *bytes = (size_t)ws_layout(d, n).bytes;
-    return MOE_OK;
-}
-
-namespace {
-
-// One GEMM1 call: the pre-pass (row-scale table and tile descriptors) and the
-// main kernel; q_scale and w_scale are fp32 scales or packed e8m0 codes (MX).
-template <bool MX>
-moe_status run_gemm1(const moe_dims* dims, int32_t n, const uint8_t* q_e4m3, const uint32_t* q_scale,
-                     const int32_t* row_slot, const int32_t* expert_offsets, const uint8_t* w_e4m3,
-                     const void* w_scale, uint16_t* y_bf16, void* ws, size_t ws_bytes, void* hip_stream) {
-    moe::Dims d;
-    moe_status st = moe::load_dims(dims, &d, true);
-    if (st != MOE_OK) return st;
-    if (n < 128 || n % 128 != 0) return MOE_ERR_INVALID_ARG;
+// One grouped-GEMM call: y[r, c] = sum_k A[r, k] * B[e(r), c, k], K = kdim,
+// c < n, for the rows_cap-capacity expert-major rows.  A row r is q[row_slot[r]]
+// (q has a_rows rows) or, with DIRECT, q[r].  q_scale and w_scale are fp32
+// scales or packed e8m0 codes (MX).  Row weights (row_assign, topk_w) scale
+// each row's output (fp32 path only).
+template <bool MX, bool DIRECT>
+moe_status run_gemm(const moe::Dims& d, int64_t a_rows, int64_t kdim, int64_t n, const uint8_t* q_e4m3,
+                    const uint32_t* q_scale, const int32_t* row_slot, const int32_t* row_assign,
+                    const float* topk_w, const int32_t* expert_offsets, const uint8_t* w_e4m3,
+                    const void* w_scale, uint16_t* y_bf16, void* ws, size_t ws_bytes, void* hip_stream) {
+    static_assert(!(MX && DIRECT), "no MX GEMM2");
+    if (n < 128 || n % 128 != 0 || kdim < 128 || kdim % 128 != 0) return MOE_ERR_INVALID_ARG;
     if (d.L > kMaxL) return MOE_ERR_UNSUPPORTED;
     if (d.T == 0) return MOE_OK;
-    if (!q_e4m3 || !q_scale || !row_slot || !expert_offsets || !w_e4m3 || !w_scale || !y_bf16)
+    if (!q_e4m3 || !q_scale || (!DIRECT && !row_slot) || !expert_offsets || !w_e4m3 || !w_scale || !y_bf16)
         return MOE_ERR_INVALID_ARG;
+    if ((topk_w != nullptr) != (row_assign != nullptr)) return MOE_ERR_INVALID_ARG;
     const int64_t rows_cap = d.T * d.k;
-    // 32-bit offsets inside the kernel: slot rows of q, rows of one expert's weight;
+    // 32-bit offsets inside the kernel: rows of q, rows of one expert's weight;
     // row tile ids in 22 bits of a descriptor
-    if (d.T * d.H >= ((int64_t)1 << 32) || (int64_t)n * d.H >= ((int64_t)1 << 31) ||
+    if (a_rows * kdim >= ((int64_t)1 << 32) || n * kdim >= ((int64_t)1 << 31) ||
         rows_cap * n >= ((int64_t)1 << 40) || rows_cap / kMinBM >= ((int64_t)1 << 22))
         return MOE_ERR_UNSUPPORTED;
-    const int64_t KB = d.H / BK;
-    const WsLayout wl = ws_layout(d, n);
+    const int64_t KB = kdim / BK;
+    const WsLayout wl = ws_layout(rows_cap, KB, n, d.L);
     if (!ws || ws_bytes < (size_t)wl.bytes) return MOE_ERR_WORKSPACE;
     if (KB * wl.scale_ld >= ((int64_t)1 << 31) || wl.tiles_cap >= ((int64_t)1 << 31) - 1)
         return MOE_ERR_UNSUPPORTED;
@@ -569,18 +578,30 @@ moe_status run_gemm1(const moe_dims* dims, int32_t n, const uint8_t* q_e4m3, con
     // gather workgroups plus the planning workgroup (the last one)
     const int64_t KG = (KB + kPrepKb - 1) / kPrepKb;
     const int pgrid = (int)std::min<int64_t>((rows_cap * KG + 255) / 256, 4096) + 1;
-    hipLaunchKernelGGL((gemm1_prep_kernel<TileCfg::BM>), dim3(pgrid), dim3(256), 0, stream, q_scale, row_slot,
-                       expert_offsets, (int)d.L, (int)KB, NT, d.T, rows_cap, wl.scale_ld, row_scale, tiles,
-                       wl.tiles_cap);
+    hipLaunchKernelGGL((gemm1_prep_kernel<TileCfg::BM>), dim3(pgrid), dim3(256), 0, stream, q_scale,
+                       DIRECT ? nullptr : row_slot, row_assign, topk_w, rows_cap, expert_offsets, (int)d.L,
+                       (int)KB, NT, a_rows, rows_cap, wl.scale_ld, row_scale, tiles, wl.tiles_cap);
+    moe_status st;
     if ((st = moe::launch_status()) != MOE_OK) return st;
     const int grid = ((cus + kXcds - 1) / kXcds) * kXcds;
-    hipLaunchKernelGGL((grouped_gemm1_kernel<TileCfg, MX>), dim3(grid), dim3(TileCfg::kThreads), 0, stream,
-                       q_e4m3, row_scale, tiles, row_slot, w_e4m3, w_scale, y_bf16, (int)n, (int)d.H, d.T,
-                       wl.scale_ld);
+    hipLaunchKernelGGL((grouped_gemm1_kernel<TileCfg, MX, DIRECT>), dim3(grid), dim3(TileCfg::kThreads), 0,
+                       stream, q_e4m3, row_scale, tiles, row_slot, w_e4m3, w_scale, y_bf16, (int)n, (int)kdim,
+                       a_rows, wl.scale_ld);
     return moe::launch_status();
 }
 
+moe_status load(const moe_dims* dims, moe::Dims* d) { return moe::load_dims(dims, d, true); }
+
 }  // namespace
+
+extern "C" moe_status moe_grouped_gemm1_workspace(const moe_dims* dims, int32_t n, size_t* bytes) {
+    moe::Dims d;
+    moe_status st = load(dims, &d);
+    if (st != MOE_OK) return st;
+    if (!bytes || n < 128 || n % 128 != 0) return MOE_ERR_INVALID_ARG;
+    *bytes = (size_t)ws_layout(d.T * d.k, d.H / BK, n, d.L).bytes;
+    return MOE_OK;
+}
 
 extern "C" moe_status moe_grouped_gemm1(const moe_dims* dims, int32_t n, const uint8_t* q_e4m3,
                                         const float* q_scale, const int32_t* row_slot,
@@ -588,8 +609,12 @@ extern "C" moe_status moe_grouped_gemm1(const moe_dims* dims, int32_t n, const u
                                         const uint8_t* w_e4m3, const float* w_scale, uint16_t* y_bf16,
                                         void* ws, size_t ws_bytes, void* hip_stream) {
     (void)totals;
-    return run_gemm1<false>(dims, n, q_e4m3, reinterpret_cast<const uint32_t*>(q_scale), row_slot,
-                            expert_offsets, w_e4m3, w_scale, y_bf16, ws, ws_bytes, hip_stream);
+    moe::Dims d;
+    moe_status st = load(dims, &d);
+    if (st != MOE_OK) return st;
+    return run_gemm<false, false>(d, d.T, d.H, n, q_e4m3, reinterpret_cast<const uint32_t*>(q_scale), row_slot,
+                                  nullptr, nullptr, expert_offsets, w_e4m3, w_scale, y_bf16, ws, ws_bytes,
+                                  hip_stream);
 }
 
 extern "C" moe_status moe_grouped_gemm1_mx(const moe_dims* dims, int32_t n, const uint8_t* q_e4m3,
@@ -597,6 +622,32 @@ extern "C" moe_status moe_grouped_gemm1_mx(const moe_dims* dims, int32_t n, cons
                                            const int32_t* expert_offsets, const uint8_t* w_e4m3,
                                            const uint32_t* w_scale, uint16_t* y_bf16, void* ws,
                                            size_t ws_bytes, void* hip_stream) {
-    return run_gemm1<true>(dims, n, q_e4m3, q_scale, row_slot, expert_offsets, w_e4m3, w_scale, y_bf16, ws,
-                           ws_bytes, hip_stream);
+    moe::Dims d;
+    moe_status st = load(dims, &d);
+    if (st != MOE_OK) return st;
+    return run_gemm<true, false>(d, d.T, d.H, n, q_e4m3, q_scale, row_slot, nullptr, nullptr, expert_offsets,
+                                 w_e4m3, w_scale, y_bf16, ws, ws_bytes, hip_stream);
+}
+
+extern "C" moe_status moe_grouped_gemm2_workspace(const moe_dims* dims, int32_t inter, size_t* bytes) {
+    moe::Dims d;
+    moe_status st = load(dims, &d);
+    if (st != MOE_OK) return st;
+    if (!bytes || inter < 128 || inter % 128 != 0) return MOE_ERR_INVALID_ARG;
+    *bytes = (size_t)ws_layout(d.T * d.k, inter / BK, d.H, d.L).bytes;
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_grouped_gemm2(const moe_dims* dims, int32_t inter, const uint8_t* h_e4m3,
+                                        const float* h_scale, const int32_t* expert_offsets,
+                                        const int32_t* row_assign, const float* topk_w,
+                                        const uint8_t* w2_e4m3, const float* w2_scale, uint16_t* y2_bf16,
+                                        void* ws, size_t ws_bytes, void* hip_stream) {
+    moe::Dims d;
+    moe_status st = load(dims, &d);
+    if (st != MOE_OK) return st;
+    if (!row_assign || !topk_w) return MOE_ERR_INVALID_ARG;
+    return run_gemm<false, true>(d, d.T * d.k, inter, d.H, h_e4m3, reinterpret_cast<const uint32_t*>(h_scale),
+                                 nullptr, row_assign, topk_w, expert_offsets, w2_e4m3, w2_scale, y2_bf16, ws,
+                                 ws_bytes, hip_stream);
 }

@@ -16,17 +16,8 @@
 // without an LDS round trip (the pages needed an LDS swizzle for that because
 // their send buffer interleaved payload and scales).
 //
-// Bit-exactness: the definition is e4m3(x / s) with an IEEE division.  The
-// kernel computes w = x * (1/s) (both roundings to nearest) and encodes w with
-// the hardware conversion (v_cvt_pk_fp8_f32: OCP e4m3, round to nearest even;
-// every |w| here is below the 464 rounding boundary, so no saturation case
-// arises), unless w lies within 8 fp32 ulps of an e4m3 rounding tie, or in the
-// e4m3 subnormal range (|w| < 2^-6, nonzero): such elements (rare; the lane
-// takes one divergent branch) redo the IEEE division x / s.  Bound: 1/s and
-// the product each carry <= 2^-24 relative error, so |w - x/s| <= 2 ulp(x/s),
-// and the correctly rounded quotient is within 0.5 ulp of x/s, so outside the
-// window both round to the same code.
-#include "common.h"
+// Bit-exactness of the fp32-scale codes at multiply cost: fp8_block.h.
+#include "fp8_block.h"
 
 namespace {
 
@@ -35,39 +26,11 @@ constexpr int kWaves = kBlock / MOE_WAVE;
 // pieces per slot row: with about one row per resident wavefront, whole rows
 // leave a second, mostly empty round of rows at the end
 constexpr int kSplit = 2;
-constexpr uint32_t kMinNormalBits = 0x3C800000u;   // 2^-6, smallest e4m3 normal
-
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
-}
-
-// |max| of the 8 lanes l..l|7 (aligned groups of 8): quad_perm [1,0,3,2],
-// quad_perm [2,3,0,1], then row_half_mirror joins the two quads.
-__device__ __forceinline__ uint32_t group8_max(uint32_t v) {
-    v = max(v, dpp<0xB1>(v));
-    v = max(v, dpp<0x4E>(v));
-    v = max(v, dpp<0x141>(v));
-    return v;
-}
-
-// True when w might round differently from the IEEE quotient: within 8 ulps
-// of an e4m3 rounding tie in the normal range, or a nonzero e4m3 subnormal.
-__device__ __forceinline__ bool needs_exact(float w) {
-    const uint32_t ab = __float_as_uint(w) & 0x7FFFFFFFu;
-    const bool tie = ((ab & 0xFFFFFu) - 0x7FFF8u) < 16u;
-    const bool sub = (ab - 1u) < (kMinNormalBits - 1u);
-    return tie | sub;
-}
-
-// four e4m3 codes of (a, b, c, d), hardware round to nearest even
-__device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
-    int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-    v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
-    return (uint32_t)v;
-}
+using moe::cvt4;
+using moe::dpp;
+using moe::group8_max;
 
 __global__ void __launch_bounds__(kBlock)
 quant_dispatch_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ slot_tok,
@@ -114,36 +77,17 @@ quant_dispatch_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict_
             }
             uint32_t m = max((uint32_t)m2.x, (uint32_t)m2.y);
             m = group8_max(m);
-            const float amax = __uint_as_float(m << 16);
-            const float s = amax / 448.0f;
-            const float r = 1.0f / s;
-            const bool zero = m == 0;
-            // a scale too small for 1/s to be finite takes the exact division throughout
-            const bool all_exact = !(r <= 3.0e38f);
-            float xv[16], w[16];
-            bool slow = all_exact;
+            float xv[16];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 xv[2 * i] = moe::bf16_lo(wv[i]);
                 xv[2 * i + 1] = moe::bf16_hi(wv[i]);
             }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                w[i] = __fmul_rn(xv[i], r);
-                slow |= needs_exact(w[i]);
-            }
-            if (slow) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    if (all_exact || needs_exact(w[i])) w[i] = xv[i] / s;
-            }
             uint32_t out[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                out[i] = zero ? 0u : cvt4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+            const float s = moe::encode_block16(xv, __uint_as_float(m << 16), out);
             if (act) {
                 __builtin_nontemporal_store(moe::u32x4{out[0], out[1], out[2], out[3]}, dst + blk * 8 + sub);
-                if (sub == 0) sdst[blk] = zero ? 0.0f : s;
+                if (sub == 0) sdst[blk] = s;
             }
         }
     }

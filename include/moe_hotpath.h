@@ -215,6 +215,63 @@ moe_status moe_grouped_gemm1_mx(const moe_dims* dims, int32_t n,
                                 uint16_t* y_bf16, void* ws, size_t ws_bytes, void* hip_stream);
 
 /*
+ * Stage2 (after GEMM1), the expert MLP's second half ("poc(cco): MegaMoE
+ * stage1 dispatch over SDMA", "What": stage1's output feeds stage2 + combine;
+ * commit "recv_layout": the layout's per-row routing weights serve stage2).
+ * The pages do not state stage2's arithmetic; the reading: GEMM1's width is
+ * n = 2*inter, columns [0, inter) the gate and [inter, 2*inter) the up
+ * projection of the same row.
+ *
+ * moe_silu_mul_quant: for expert-major row r < R (R = totals[0], read on the
+ * device) and i < inter:
+ *   h[r, i] = silu(gate) * up,  silu(x) = x / (1 + e^-x), in fp32 from the
+ *   bf16 inputs (the exponential and reciprocal are the hardware's
+ *   approximations: h carries a few fp32 ulps of error);
+ * then GEMM1's quant rule per block b of 128 elements of h: s = amax / 448
+ * (IEEE), q = e4m3(h / s) (IEEE quotient, round to nearest even; exact given
+ * the kernel's h), a == 0 giving s = 0 and zero bytes.
+ * In:  y1_bf16 uint16 (bf16 bits) [rows_cap, 2*inter] (GEMM1's output);
+ *      totals from step 1.
+ * Out: h_e4m3 uint8 [rows_cap, inter]; h_scale float32 [rows_cap, inter/128].
+ * Rows past R are not written.  inter must be a positive multiple of 128.
+ */
+moe_status moe_silu_mul_quant(const moe_dims* dims, int32_t inter, const uint16_t* y1_bf16,
+                              const int32_t* totals, uint8_t* h_e4m3, float* h_scale,
+                              void* hip_stream);
+
+/* Workspace bytes moe_grouped_gemm2 needs (host-only): the K-block-major row
+ * scale table, (inter/128) x (rows_cap + 256, rounded up to 64) floats (padded
+ * to 256 B), then (1 + (rows_cap/128 + L) * ceil(H/256)) 16 B tile descriptors. */
+moe_status moe_grouped_gemm2_workspace(const moe_dims* dims, int32_t inter, size_t* bytes);
+
+/*
+ * GEMM2: the grouped down projection, each row scaled by its routing weight
+ * (the pages' per-row weights table of the layout).  For local expert le, row
+ * r in [expert_offsets[le], expert_offsets[le+1]) and column c < H:
+ *   y2[r, c] = bf16( w_r * sum_i  h[r, i] * h_scale[r, i/128]
+ *                                * w2[le, c, i] * w2_scale[le, c/128, i/128] )
+ *   w_r = topk_w[row_assign[r]]   (flat index g*k + j of the row's assignment)
+ * accumulated in fp32 (fp8 MFMA per 128-wide K block; w_r folded into the
+ * row's scales).  A rows are the expert-major rows themselves (row r reads
+ * h row r, no rowmap).
+ * In:  h_e4m3, h_scale from moe_silu_mul_quant; expert_offsets, row_assign
+ *      from step 1 (a layout of the same dims); topk_w float32 [T, k];
+ *      w2_e4m3  uint8 [L, H, inter] (element (i, c) of the logical [inter, H]
+ *               weight at [le, c, i], K-contiguous);
+ *      w2_scale float32 [L, H/128, inter/128], one per 128x128 block.
+ * Out: y2_bf16 uint16 (bf16 bits) [rows_cap, H]; rows past R are not written.
+ * ws: device workspace of at least moe_grouped_gemm2_workspace bytes.
+ * A row_assign entry outside [0, T*k) gives that row weight 0 (it cannot
+ * come from step 1).
+ */
+moe_status moe_grouped_gemm2(const moe_dims* dims, int32_t inter,
+                             const uint8_t* h_e4m3, const float* h_scale,
+                             const int32_t* expert_offsets, const int32_t* row_assign,
+                             const float* topk_w,
+                             const uint8_t* w2_e4m3, const float* w2_scale,
+                             uint16_t* y2_bf16, void* ws, size_t ws_bytes, void* hip_stream);
+
+/*
  * Step 4: combine.  Top-k weighted gather-sum back to token order (TilePipe:
  * push combine to the token owners; "MegaMoE stage1 dispatch over SDMA",
  * "What": stage2 + combine).

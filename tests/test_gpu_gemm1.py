@@ -127,7 +127,8 @@ def test_gemm1_identity_weights_bit_exact():
     rq, rs = oquant.quant_dispatch(x, ref["slot_tok"])
     A = ogemm1.dequant_rows(rq, rs)[ref["row_slot"]]
     R = int(ref["totals"][0])
-    np.testing.assert_array_equal(host_u16(y[:R]), obf16.from_f32(A))
+    # a sum of products is +0 where the lone nonzero term is -0 (the other terms add +0)
+    np.testing.assert_array_equal(host_u16(y[:R]), obf16.from_f32(A + np.float32(0)))
 
 
 def test_gemm1_permutation_weights_bit_exact():
@@ -149,4 +150,4 @@ def test_gemm1_permutation_weights_bit_exact():
     got = host_u16(y)
     for le in range(6):
         for r in range(offs[le], offs[le + 1]):
-            np.testing.assert_array_equal(got[r], obf16.from_f32(A[ref["row_slot"][r]][perms[le]]))
+            np.testing.assert_array_equal(got[r], obf16.from_f32(A[ref["row_slot"][r]][perms[le]] + np.float32(0)))

@@ -234,7 +234,8 @@ def test_gemm1_mx_identity_weights_bit_exact():
     rq, rs = omx.quant_dispatch(x, ref["slot_tok"])
     A = omx.dequant_rows(rq, rs)[ref["row_slot"]]
     R = int(ref["totals"][0])
-    np.testing.assert_array_equal(host_u16(y[:R]), obf16.from_f32(A))
+    # a sum of products is +0 where the lone nonzero term is -0 (the other terms add +0)
+    np.testing.assert_array_equal(host_u16(y[:R]), obf16.from_f32(A + np.float32(0)))
 
 
 def test_gemm1_mx_permutation_weights_bit_exact():
@@ -265,4 +266,4 @@ def test_gemm1_mx_permutation_weights_bit_exact():
         shift = codes[le, cols, perms[le] // 32].astype(np.int64) - 127
         for r in range(offs[le], offs[le + 1]):
             want = A[ref["row_slot"][r]][perms[le]] * np.ldexp(1.0, shift)
-            np.testing.assert_array_equal(got[r], obf16.from_f32(want.astype(np.float32)))
+            np.testing.assert_array_equal(got[r], obf16.from_f32(want.astype(np.float32) + np.float32(0)))
