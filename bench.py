@@ -15,7 +15,9 @@ steps, the MX-style variant of stage1 (e8m0 scales per 32 K elements: layout
 -> moe_quant_dispatch_mx -> moe_grouped_gemm1_mx) is timed on the same inputs
 in a separate A/B loop that alternates one fp32-scale stage1 step with one MX
 step (the clock drifts over a run, so only interleaved numbers compare), and
-reported under "mx".
+reported under "mx".  Stage2 on GEMM1's output (silu(gate) * up with its fp8
+quant -> grouped GEMM2 with the routing weights -> combine of the local rows)
+is timed after that and reported under "stage2".
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--no-cpu-baseline] [--copy-calib]
@@ -88,8 +90,16 @@ def algorithmic(w, R, U, Rc):
     # both operands (activations: as the fp32 scale; weights: per column)
     gemm_mx_bytes = U * (H + H // 32) + L * N * H + L * N * (H // 128) * 4 + R * N * 2
     combine = Rc * width * 2 + T * k * 8 + T * width * 2
+    # stage2: I = N/2; act reads [R, 2I] bf16, writes [R, I] fp8 + scales; GEMM2 reads
+    # h + its scales, W2 [L, H, I] + block scales and the row weights, writes [R, H]
+    I = N // 2
+    act = 8 + R * (2 * I * 2 + I + (I // 128) * 4)
+    gemm2_flop = 2 * R * I * H
+    gemm2_bytes = R * (I + I // 32) + L * H * I + L * (H // 128) * (I // 128) * 4 + R * 8 + R * H * 2
+    combine_local = R * H * 2 + T * k * 8 + T * H * 2
     return dict(layout_local=lay_local, quant=quant, gemm1_flop=gemm_flop, gemm1_bytes=gemm_bytes,
-                layout_full=lay_full, combine=combine, quant_mx=quant, gemm1_mx_bytes=gemm_mx_bytes)
+                layout_full=lay_full, combine=combine, quant_mx=quant, gemm1_mx_bytes=gemm_mx_bytes,
+                silu_mul_quant=act, gemm2_flop=gemm2_flop, gemm2_bytes=gemm2_bytes, combine_local=combine_local)
 
 
 def main():
@@ -210,6 +220,7 @@ def main():
     mx = mx_stage1(torch, moe, w, d_loc, ids_d, x_d, lay, g_ws, alg, traffic, args,
                    fp32_step=lambda: (moe.quant_dispatch(d_loc, x_d, lay, q, qs),
                                       moe.grouped_gemm1(d_loc, w.N, q, qs, lay, wq_d, ws_d, y1, g_ws)))
+    s2 = stage2(torch, moe, w, d_loc, lay, y1, wts_d, alg, traffic, args)
     ceil = ceilings(torch, moe, args.copy_calib)
 
     rec = {
@@ -229,6 +240,7 @@ def main():
         "percentiles_us": spread,
         "stage1_graph": graph,
         "mx": mx,
+        "stage2": s2,
         "ceilings": ceil,
         "fraction_of_measured_ceilings": {
             "gemm1_vs_mfma_loop": round(gemm_tflops / ceil["mfma_fp8_tflops"], 4),
@@ -303,6 +315,65 @@ def mx_stage1(torch, moe, w, d, ids_d, x_d, lay, g_ws, alg, traffic, args, fp32_
                              "unit": "TFLOP/s", "frac": round(ga / FP8_PEAK_TFLOPS, 4),
                              "traffic": traffic.get("gemm1_mx"), "algorithmic_flop": int(alg["gemm1_flop"]),
                              "algorithmic_bytes": int(alg["gemm1_mx_bytes"])}}}
+
+
+def stage2(torch, moe, w, d, lay, y1, wts_d, alg, traffic, args):
+    """Stage2 on GEMM1's output y1: silu_mul_quant -> GEMM2 (routing weights
+    applied) -> combine of the local rows with unit weights; `warmup` untimed
+    then `steps` timed, HIP events between the calls."""
+    import workloads
+    t0 = time.time()
+    w2, w2s = workloads.weights2(w)
+    log(f"[bench] GEMM2 weights generated in {time.time() - t0:.1f}s")
+    w2_d, w2s_d = torch.from_numpy(w2).cuda(), torch.from_numpy(w2s).cuda()
+    del w2, w2s
+    I = w.N // 2
+    rows_cap = w.T * w.k
+    h = torch.empty((rows_cap, I), dtype=torch.uint8, device="cuda")
+    hs = torch.empty((rows_cap, I // 128), dtype=torch.float32, device="cuda")
+    y2 = torch.empty((rows_cap, w.H), dtype=torch.bfloat16, device="cuda")
+    g2_ws = moe.alloc_gemm2_workspace(d, I)
+    out = torch.empty((w.T, w.H), dtype=torch.bfloat16, device="cuda")
+    ones = torch.ones(rows_cap, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    names = ["silu_mul_quant", "gemm2", "combine_local"]
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        moe.silu_mul_quant(d, I, y1, lay, h, hs)
+        if ev: ev[1].record(stream)
+        moe.grouped_gemm2(d, I, h, hs, lay, wts_d, w2_d, w2s_d, y2, g2_ws)
+        if ev: ev[2].record(stream)
+        moe.combine(d, w.H, y2, lay["assign_row"], ones, out)
+        if ev: ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    per = {n: [e[j].elapsed_time(e[j + 1]) * 1e3 for e in evs] for j, n in enumerate(names)}
+    med = {n: float(np.median(v)) for n, v in per.items()}
+    tot = [sum(per[n][i] for n in names) for i in range(args.steps)]
+
+    def hbm(n, key):
+        a = alg[key] / (med[n] * 1e-6) / 1e9
+        return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(a / HBM_PEAK_GBS, 4), "traffic": traffic.get(n), "algorithmic_bytes": int(alg[key])}
+
+    ga = alg["gemm2_flop"] / (med["gemm2"] * 1e-6) / 1e12
+    del w2_d, w2s_d, h, hs, y2, out
+    return {"us_median": round(float(np.median(tot)), 2),
+            "us_p10_p90": [round(float(np.percentile(tot, 10)), 2), round(float(np.percentile(tot, 90)), 2)],
+            "inter": I, "kernels_us_median": {n: round(med[n], 2) for n in names},
+            "kernels": {"silu_mul_quant": hbm("silu_mul_quant", "silu_mul_quant"),
+                        "gemm2": {"bound": "mfma", "achieved": round(ga, 1), "peak": FP8_PEAK_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": round(ga / FP8_PEAK_TFLOPS, 4),
+                                  "traffic": traffic.get("gemm2"), "algorithmic_flop": int(alg["gemm2_flop"]),
+                                  "algorithmic_bytes": int(alg["gemm2_bytes"])},
+                        "combine_local": hbm("combine_local", "combine_local")}}
 
 
 def stage1_graph(torch, moe, d, ids_d, x_d, wq_d, ws_d, lay, q, qs, y1, g_ws, w, R, U, steps):

@@ -382,19 +382,34 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
                     for (int v = 0; v < 4; ++v) acc[i][NJ - 1][v] = fmaf(pp[i][v], f[i], acc[i][NJ - 1][v]);
             }
         }
-        // epilogue: bf16 (RNE), valid rows and columns only
+        // epilogue: bf16 (RNE), valid rows only.  Each 16 x 64 piece (one row group
+        // of this wavefront's columns) goes through LDS so that the global stores
+        // write whole 128 B rows, 8 lanes x 16 B per row (written straight from the
+        // MFMA layout, a lane's 8 B pieces would land as 32 B slivers of 16 rows per
+        // store instruction).  Staging: 2 KB per wavefront in the ring slot of the
+        // tile's last K step, which the loaders refill only after the next barrier,
+        // one these wavefronts have not reached yet; 16 B chunks XOR-swizzled by row.
+        static_assert(C::CW == 64 && C::kCompute * 2048 <= STAGE, "epilogue staging: 128 B rows, 2 KB a wavefront");
         if (active) {
+            uint8_t* stg = ring + ((g - 1) % NSTAGE) * STAGE + wave * 2048;
+            const int srow = lane & 15, q = lane >> 4;
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
-                const int row = wm * RW + i * 16 + (lane & 15);
-                if (row < nvalid) {
-                    uint16_t* yrow = y + (int64_t)(r0 + row) * N + n0 + wn * CW + 4 * (lane >> 4);
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) {
-                        const uint32_t lo = moe::f32_to_bf16_rne(acc[i][j][0]) | (moe::f32_to_bf16_rne(acc[i][j][1]) << 16);
-                        const uint32_t hi = moe::f32_to_bf16_rne(acc[i][j][2]) | (moe::f32_to_bf16_rne(acc[i][j][3]) << 16);
-                        *reinterpret_cast<uint2*>(yrow + j * 16) = make_uint2(lo, hi);
-                    }
+                for (int j = 0; j < NJ; ++j) {
+                    const uint32_t lo = moe::f32_to_bf16_rne(acc[i][j][0]) | (moe::f32_to_bf16_rne(acc[i][j][1]) << 16);
+                    const uint32_t hi = moe::f32_to_bf16_rne(acc[i][j][2]) | (moe::f32_to_bf16_rne(acc[i][j][3]) << 16);
+                    // columns j*16 + 4q .. +3 = byte 32j + 8q of the 128 B row: chunk 2j + q/2
+                    *reinterpret_cast<uint2*>(stg + srow * 128 + (((2 * j + (q >> 1)) ^ (srow & 7)) << 4) + (q & 1) * 8) =
+                        make_uint2(lo, hi);
+                }
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    const int rr = p * 8 + (lane >> 3), c = lane & 7;
+                    const moe::u32x4 v = *reinterpret_cast<const moe::u32x4*>(stg + rr * 128 + ((c ^ (rr & 7)) << 4));
+                    const int row = wm * RW + i * 16 + rr;
+                    if (row < nvalid)
+                        *reinterpret_cast<moe::u32x4*>(y + (int64_t)(r0 + row) * N + n0 + wn * CW + c * 8) = v;
                 }
             }
         }
