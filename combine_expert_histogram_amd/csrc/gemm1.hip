@@ -661,7 +661,7 @@ extern "C" moe_status moe_grouped_gemm2(const moe_dims* dims, int32_t inter, con
     moe::Dims d;
     moe_status st = load(dims, &d);
     if (st != MOE_OK) return st;
-    if (!row_assign || !topk_w) return MOE_ERR_INVALID_ARG;
+    if (d.T != 0 && (!row_assign || !topk_w)) return MOE_ERR_INVALID_ARG;
     return run_gemm<false, true>(d, d.T * d.k, inter, d.H, h_e4m3, reinterpret_cast<const uint32_t*>(h_scale),
                                  nullptr, row_assign, topk_w, expert_offsets, w2_e4m3, w2_scale, y2_bf16, ws,
                                  ws_bytes, hip_stream);

@@ -108,3 +108,40 @@ def test_empty_input_calls_are_noops(L):
     assert L.moe_quant_dispatch(ctypes.byref(d), None, None, None, None, None, None) == 0
     assert L.moe_grouped_gemm1(ctypes.byref(d), 256, *([None] * 8), None, 0, None) == 0
     assert L.moe_combine(ctypes.byref(d), 256, None, 0, None, None, None, None) == 0
+
+
+def test_stage2_and_mx_workspaces(L):
+    from combine_expert_histogram_amd import binding as b
+    d = b.Dims(S=8, Ts=2048, k=8, E=256, e0=0, L=32, H=7168)
+    # GEMM2: K = inter, n = H; the same table + descriptor layout as GEMM1's
+    inter = 2048
+    table = ((inter // 128) * ((16384 * 8 + 256 + 63) // 64 * 64) * 4 + 255) // 256 * 256
+    assert b.moe_grouped_gemm2_workspace(d, inter) == table + (1 + (16384 * 8 // 128 + 32) * (7168 // 256)) * 16
+    for bad in (0, 64, 200):
+        with pytest.raises(b.MoeError):
+            b.moe_grouped_gemm2_workspace(d, bad)
+
+
+def test_stage2_and_mx_validation_before_any_launch(L):
+    from combine_expert_histogram_amd import binding as b
+    d = b.Dims(S=1, Ts=64, k=2, E=8, e0=0, L=8, H=256).c()
+    fake = ctypes.c_void_p(4096)   # never dereferenced: validation fails first
+    assert L.moe_quant_dispatch_mx(ctypes.byref(d), None, fake, fake, fake, fake, None) == -1
+    assert L.moe_grouped_gemm1_mx(ctypes.byref(d), 256, *([None] * 7), None, 0, None) == -1
+    assert L.moe_grouped_gemm1_mx(ctypes.byref(d), 200, *([fake] * 7), fake, 1 << 30, None) == -1   # n % 128
+    assert L.moe_silu_mul_quant(ctypes.byref(d), 100, fake, fake, fake, fake, None) == -1          # inter % 128
+    assert L.moe_silu_mul_quant(ctypes.byref(d), 128, None, fake, fake, fake, None) == -1
+    # GEMM2 needs the row weights (row_assign and topk_w)
+    args = [fake, fake, fake, None, fake, fake, fake, fake]
+    assert L.moe_grouped_gemm2(ctypes.byref(d), 128, *args, fake, 1 << 30, None) == -1
+    # a short workspace
+    assert L.moe_grouped_gemm2(ctypes.byref(d), 128, *([fake] * 8), fake, 16, None) == -2
+
+
+def test_stage2_and_mx_empty_input_calls_are_noops(L):
+    from combine_expert_histogram_amd import binding as b
+    d = b.Dims(S=2, Ts=0, k=2, E=8, e0=0, L=8, H=256).c()
+    assert L.moe_quant_dispatch_mx(ctypes.byref(d), None, None, None, None, None, None) == 0
+    assert L.moe_grouped_gemm1_mx(ctypes.byref(d), 256, *([None] * 7), None, 0, None) == 0
+    assert L.moe_silu_mul_quant(ctypes.byref(d), 128, None, None, None, None, None) == 0
+    assert L.moe_grouped_gemm2(ctypes.byref(d), 128, *([None] * 8), None, 0, None) == 0
