@@ -214,8 +214,9 @@ def main():
     spread = {n: {"p10": round(pct(per[n], 10), 2), "p90": round(pct(per[n], 90), 2)} for n in names}
     spread["stage1"] = {"p10": round(pct(stage1_all, 10), 2), "p90": round(pct(stage1_all, 90), 2)}
 
-    # stage1 (layout -> quant -> GEMM1) captured once in a graph and replayed; the
-    # calls read their counts on the device, so the capture needs no host sync
+    # stage1 (layout -> quant -> GEMM1) captured once in a graph and replayed beside
+    # eager steps; the calls read their counts on the device, so the capture needs
+    # no host sync
     graph = stage1_graph(torch, moe, d_loc, ids_d, x_d, wq_d, ws_d, lay, q, qs, y1, g_ws, w, R, U, args.steps)
     mx = mx_stage1(torch, moe, w, d_loc, ids_d, x_d, lay, g_ws, alg, traffic, args,
                    fp32_step=lambda: (moe.quant_dispatch(d_loc, x_d, lay, q, qs),
@@ -378,39 +379,47 @@ def stage2(torch, moe, w, d, lay, y1, wts_d, alg, traffic, args):
 
 def stage1_graph(torch, moe, d, ids_d, x_d, wq_d, ws_d, lay, q, qs, y1, g_ws, w, R, U, steps):
     """Captures layout -> quant -> GEMM1 into one graph (all buffers preallocated),
-    replays it `steps` times back to back (events between the replays, on the
-    replay stream) and checks the graph's outputs against the eager step's."""
+    checks the graph's outputs against the eager step's, then times `steps`
+    pairs of one eager stage1 step and one replay, alternating on the same
+    stream (the clock drifts over a run, so only interleaved numbers compare)."""
     ref_lay = {k: v.clone() for k, v in lay.items() if k != "ws"}
     ref_q, ref_qs, ref_y = q[:U].clone(), qs[:U].clone(), y1[:R].clone()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(s):
-        moe.route_layout(d, ids_d, lay)                      # warm the stream before capture
+
+    def eager():
+        moe.route_layout(d, ids_d, lay)
         moe.quant_dispatch(d, x_d, lay, q, qs)
         moe.grouped_gemm1(d, w.N, q, qs, lay, wq_d, ws_d, y1, g_ws)
+
+    with torch.cuda.stream(s):
+        eager()                                              # warm the stream before capture
         s.synchronize()
         with torch.cuda.graph(g, stream=s):
-            moe.route_layout(d, ids_d, lay)
-            moe.quant_dispatch(d, x_d, lay, q, qs)
-            moe.grouped_gemm1(d, w.N, q, qs, lay, wq_d, ws_d, y1, g_ws)
+            eager()
     torch.cuda.synchronize()
     for _ in range(3):
         g.replay()
     torch.cuda.synchronize()
-    # back to back, like the eager steps: an event between consecutive replays
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    with torch.cuda.stream(s):
-        for i in range(steps):
-            ev[i].record(s)
-            g.replay()
-        ev[steps].record(s)
-    torch.cuda.synchronize()
-    times = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps)]
     same = (all(torch.equal(lay[k], v) for k, v in ref_lay.items()) and torch.equal(q[:U], ref_q)
             and torch.equal(qs[:U], ref_qs) and torch.equal(y1[:R], ref_y))
-    return {"us_median": round(float(np.median(times)), 2), "us_p10": round(float(np.percentile(times, 10)), 2),
-            "us_p90": round(float(np.percentile(times, 90)), 2), "replays": steps, "matches_eager": bool(same)}
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    with torch.cuda.stream(s):
+        for i in range(steps):
+            ev[i][0].record(s)
+            eager()
+            ev[i][1].record(s)
+            g.replay()
+            ev[i][2].record(s)
+    torch.cuda.synchronize()
+    t_e = [e[0].elapsed_time(e[1]) * 1e3 for e in ev]
+    t_g = [e[1].elapsed_time(e[2]) * 1e3 for e in ev]
+    med = lambda v: round(float(np.median(v)), 2)
+    return {"us_median": med(t_g), "us_p10": round(float(np.percentile(t_g, 10)), 2),
+            "us_p90": round(float(np.percentile(t_g, 90)), 2), "eager_us_median_same_loop": med(t_e),
+            "graph_over_eager": round(float(np.median(t_g)) / float(np.median(t_e)), 4),
+            "replays": steps, "matches_eager": bool(same)}
 
 
 def ceilings(torch, moe, copy_calib):
