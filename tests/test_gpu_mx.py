@@ -51,6 +51,7 @@ def _compare_quant(ref_lay, q, qs, x_bits, slots):
 
 @pytest.mark.parametrize("name,sample", [
     ("tiny_t64_h256_e8", None), ("ep8_256x8_h7168", None), ("ep8_2048x8_h7168", 768),
+    ("ep8_8192x8_h7168_zipf", 512),
 ])
 def test_quant_mx_workloads(name, sample):
     require_gpu()
@@ -168,6 +169,7 @@ def _check_gemm(d, n, ids, x, wq, ws, sample=None):
 
 @pytest.mark.parametrize("name,sample", [
     ("tiny_t64_h256_e8", None), ("ep8_256x8_h7168", None), ("ep8_2048x8_h7168", 384),
+    ("ep8_8192x8_h7168_zipf", 384),
 ])
 def test_gemm1_mx_workloads(name, sample):
     require_gpu()
