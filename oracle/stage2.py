@@ -20,6 +20,11 @@ arithmetic.  The readings taken (plain gated-MLP expert):
     [L, H, I] bytes with one fp32 scale per 128(H) x 128(I) block;
       y2[r, c] = w_r * sum_i deq(q2[r, i]) * deq(w2[le, c, i]),  c < H,
     w_r = topk_w.flat[row_assign[r]] (the row's routing weight); float32.
+  * MX variant (the pages' own e8m0 format, as oracle.mx): h quantised with
+    power-of-two scales per 32 elements (oracle.mx.quantise_rows); GEMM2's
+    weights likewise per column and group, codes stored [L, I/128, H]; the
+    routing weight multiplies the float32 sum (it is not a power of two, so it
+    cannot ride in an e8m0 code).
   * The combine then sums the weighted rows back per token:
       out[g, c] = sum_j y2[assign_row[g*k + j], c]  (local rows only),
     i.e. oracle.combine with unit weights: the share of each token's output
@@ -29,7 +34,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import bf16, combine, gemm1, quant
+from . import bf16, combine, gemm1, mx, quant
 
 
 def silu_mul(y1_f32: np.ndarray) -> np.ndarray:
@@ -77,3 +82,24 @@ def combine_rows(y2_bf16_bits: np.ndarray, assign_row: np.ndarray, T: int, k: in
     """(acc float32, out bf16 bits) [n, H]: per token, the sum of its local rows
     of y2 (the weights were applied in GEMM2), i.e. the combine with unit weights."""
     return combine.combine(y2_bf16_bits, assign_row, np.ones(T * k, np.float32), T, k, tokens=tokens)
+
+
+def act_quant_mx(y1_bf16_bits: np.ndarray):
+    """MX variant: (q2 uint8 [n, I], packed e8m0 codes uint32 [n, I/128])."""
+    return mx.quantise_rows(silu_mul(bf16.to_f32(np.asarray(y1_bf16_bits))))
+
+
+def grouped_gemm2_mx(q2, s2, expert_offsets, row_assign, topk_w, w2, w2_scale, rows=None,
+                     q_index=None) -> np.ndarray:
+    """MX GEMM2: as grouped_gemm2 with e8m0 group scales (oracle.mx's GEMM1
+    definition on the expert-major rows): s2 uint32 [., I/128], w2 uint8
+    [L, H, I], w2_scale uint32 [L, I/128, H].  Float32 [len(rows), H]."""
+    offs = np.asarray(expert_offsets, dtype=np.int64)
+    R = int(offs[-1])
+    rows = np.arange(R) if rows is None else np.asarray(rows, dtype=np.int64)
+    rowmap = np.arange(max(R, 1))
+    if q_index is not None:
+        rowmap[rows] = np.asarray(q_index, dtype=np.int64)
+    y = mx.grouped_gemm1(q2, s2, rowmap, offs, w2, w2_scale, rows=rows)
+    w = row_weights(np.asarray(row_assign)[rows], topk_w) if rows.size else np.zeros(0, np.float32)
+    return (y * w[:, None]).astype(np.float32)

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import bf16, fp8, quant, stage2
+from oracle import bf16, fp8, mx, quant, stage2
 
 
 def test_silu_closed_forms_and_halves():
@@ -129,3 +129,61 @@ def test_combine_rows_is_the_unweighted_sum_brute_force():
             if r >= 0:
                 want += bf16.to_f32(y2[r]).astype(np.float64)
         np.testing.assert_allclose(acc[g], want, rtol=1e-6, atol=1e-6)
+
+
+def test_act_quant_mx_is_mx_quant_of_silu_mul():
+    rng = np.random.default_rng(11)
+    y = bf16.from_f32((rng.standard_normal((7, 256)) * 1.7).astype(np.float32))
+    q2, s2 = stage2.act_quant_mx(y)
+    q, s = mx.quantise_rows(stage2.silu_mul(bf16.to_f32(y)))
+    assert np.array_equal(q2, q) and np.array_equal(s2, s)
+    assert s2.dtype == np.uint32 and s2.shape == (7, 1)          # I = 128: one packed dword a row
+
+
+def test_gemm2_mx_matches_float64_triple_loop():
+    rng = np.random.default_rng(12)
+    L, H, I, R = 2, 128, 128, 5
+    offs = np.array([0, 3, 5])
+    y1 = bf16.from_f32((rng.standard_normal((R, 2 * I)) * 1.7).astype(np.float32))
+    q2, s2 = stage2.act_quant_mx(y1)
+    wf = bf16.to_f32(bf16.from_f32((rng.standard_normal((L * H, I)) * 0.02).astype(np.float32)))
+    wq, wsc = mx.quantise_rows(wf)
+    w2 = wq.reshape(L, H, I)
+    w2s = np.ascontiguousarray(wsc.reshape(L, H, I // 128).transpose(0, 2, 1))
+    T, k = 3, 2
+    topk_w = rng.uniform(0.05, 1.0, (T, k)).astype(np.float32)
+    row_assign = np.array([5, 2, 0, 4, 1])
+    y2 = stage2.grouped_gemm2_mx(q2, s2, offs, row_assign, topk_w, w2, w2s)
+    codes_a = mx.unpack_codes(s2).astype(int) - 127
+    for r in range(R):
+        le = 0 if r < 3 else 1
+        wr = float(topk_w.reshape(-1)[row_assign[r]])
+        codes_b = mx.unpack_codes(w2s[le].T).astype(int) - 127          # [H, I/32]
+        for c in range(0, H, 9):
+            acc = 0.0
+            for i in range(I):
+                a = float(fp8.decode(q2[r, i])) * 2.0 ** codes_a[r, i // 32]
+                b = float(fp8.decode(w2[le, c, i])) * 2.0 ** codes_b[c, i // 32]
+                acc += a * b
+            assert math.isclose(y2[r, c], wr * acc, rel_tol=1e-5, abs_tol=1e-6 * max(1.0, abs(acc)))
+
+
+def test_generated_gemm2_weights_follow_the_rules():
+    """workloads.weights2 (fp32 block scales) and weights2_mx (e8m0 groups) against
+    the oracle's own quantisers applied to the same bf16 draws."""
+    import workloads
+    w = workloads.get("tiny_t64_h256_e8")
+    I = w.N // 2
+    wq, ws = workloads.weights2(w, experts=range(2))
+    mq, ms = workloads.weights2_mx(w, experts=range(2))
+    for i in range(2):
+        g = np.random.default_rng(np.random.SeedSequence(w.seed).spawn(6)[4].spawn(w.L)[i])
+        wf = g.standard_normal(size=(w.H, I), dtype=np.float32) * np.float32(0.02)
+        wf = bf16.to_f32(bf16.from_f32(wf))
+        q, sc = mx.quantise_rows(wf)
+        assert np.array_equal(mq[i], q) and np.array_equal(ms[i], sc.T)
+        # fp32 128x128 block scales: scale = block |max| / 448, payload decodes within half a step
+        blk = np.abs(wf).reshape(w.H // 128, 128, I // 128, 128).max(axis=(1, 3)) / np.float32(448)
+        assert np.array_equal(ws[i], blk.astype(np.float32))
+        deq = fp8.decode(wq[i]).astype(np.float64) * np.repeat(np.repeat(ws[i], 128, 0), 128, 1)
+        assert np.all(np.abs(deq - wf) <= np.abs(wf) * 2.0 ** -4 + np.repeat(np.repeat(ws[i], 128, 0), 128, 1) * 2.0 ** -10)

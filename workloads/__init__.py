@@ -28,7 +28,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "get", "routing", "activations", "weights",
-    "expert_outputs", "weights2", "stage2_inputs", "sha256",
+    "expert_outputs", "weights2", "stage2_inputs", "weights_mx", "weights2_mx", "sha256",
 ]
 
 
@@ -240,34 +240,50 @@ def sha256(a: np.ndarray) -> str:
 def weights_mx(w: Workload, experts: range | None = None):
     """GEMM1 weights in the MX-style format: the same fp32 N(0, 0.02) -> bf16
     draws as ``weights``, quantised per column n and group of 32 consecutive K
-    elements with a power-of-two scale: E = ceil(log2(group |max| / 448))
-    (the fp32 quotient's binary exponent; an all-zero group gets E = -127),
-    payload = e4m3(value * 2^-E) (torch's float8_e4m3fn cast; exact scaling,
-    every magnitude <= 448).  The e8m0 codes E + 127 are packed four per
-    uint32 (group 4kb+g in byte g) and stored K-block-major.
+    elements with a power-of-two scale (see ``_mx_weights``).
 
     Returns (w_e4m3 uint8 [L', N, H], w_scale uint32 [L', H/128, N]).
     """
+    return _mx_weights(_stream(w.seed, "weights"), w.L, w.N, w.H, experts)
+
+
+def weights2_mx(w: Workload, experts: range | None = None):
+    """GEMM2 weights in the MX-style format: the same draws as ``weights2``.
+
+    Returns (w2_e4m3 uint8 [L', H, I], w2_scale uint32 [L', I/128, H]).
+    """
+    assert w.N % 256 == 0, "GEMM1 width must be 2*I with I a multiple of 128"
+    return _mx_weights(_stream(w.seed, "weights2"), w.L, w.H, w.N // 2, experts)
+
+
+def _mx_weights(ss: np.random.SeedSequence, L: int, N: int, K: int, experts):
+    """[L', N, K] e4m3 bytes + [L', K/128, N] packed e8m0 codes.  Expert le is
+    drawn from its own spawned seed as in ``_block_fp8_weights``: fp32
+    N(0, 0.02) -> bf16; per column n and group of 32 consecutive K elements,
+    E = ceil(log2(group |max| / 448)) (the fp32 quotient's binary exponent; an
+    all-zero group gets E = -127), payload = e4m3(value * 2^-E) (torch's
+    float8_e4m3fn cast; exact scaling, every magnitude <= 448).  The codes
+    E + 127 are packed four per uint32 (group 4kb+g in byte g) and stored
+    K-block-major."""
     import torch
-    L, N, H = w.L, w.N, w.H
     experts = range(L) if experts is None else experts
-    seeds = _stream(w.seed, "weights").spawn(L)
-    q = np.empty((len(experts), N, H), dtype=np.uint8)
-    sc = np.empty((len(experts), H // 128, N), dtype=np.uint32)
+    seeds = ss.spawn(L)
+    q = np.empty((len(experts), N, K), dtype=np.uint8)
+    sc = np.empty((len(experts), K // 128, N), dtype=np.uint32)
 
     def one(i_le):
         i, le = i_le
         g = np.random.default_rng(seeds[le])
-        wf = g.standard_normal(size=(N, H), dtype=np.float32)
+        wf = g.standard_normal(size=(N, K), dtype=np.float32)
         wf *= np.float32(0.02)
-        t = torch.from_numpy(wf).to(torch.bfloat16).to(torch.float32).view(N, H // 32, 32)
+        t = torch.from_numpy(wf).to(torch.bfloat16).to(torch.float32).view(N, K // 32, 32)
         amax = t.abs().amax(dim=2)
         m, e = torch.frexp(amax / torch.tensor(448.0, dtype=torch.float32))
         E = torch.where(m == 0.5, e - 1, e).to(torch.int64)
         E = torch.where(amax == 0, torch.full_like(E, -127), E).clamp(-127, 127)
         v = torch.ldexp(t.to(torch.float64), (-E)[:, :, None].to(torch.float64)).to(torch.float32)
-        q[i] = v.to(torch.float8_e4m3fn).view(torch.uint8).reshape(N, H).numpy()
-        c = (E + 127).to(torch.int64).view(N, H // 128, 4)
+        q[i] = v.to(torch.float8_e4m3fn).view(torch.uint8).reshape(N, K).numpy()
+        c = (E + 127).to(torch.int64).view(N, K // 128, 4)
         packed = c[..., 0] | (c[..., 1] << 8) | (c[..., 2] << 16) | (c[..., 3] << 24)
         sc[i] = packed.t().numpy().astype(np.uint32)
 
