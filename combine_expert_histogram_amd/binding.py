@@ -24,7 +24,8 @@ _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_WORKSPACE",
 EXPORTS = ("moe_status_string", "moe_capacity", "moe_route_layout_workspace", "moe_route_layout",
            "moe_quant_dispatch", "moe_grouped_gemm1_workspace", "moe_grouped_gemm1",
            "moe_quant_dispatch_mx", "moe_grouped_gemm1_mx", "moe_silu_mul_quant",
-           "moe_grouped_gemm2_workspace", "moe_grouped_gemm2", "moe_combine")
+           "moe_grouped_gemm2_workspace", "moe_grouped_gemm2", "moe_silu_mul_quant_mx",
+           "moe_grouped_gemm2_mx", "moe_combine")
 
 
 class MoeError(RuntimeError):
@@ -84,6 +85,8 @@ def lib() -> ctypes.CDLL:
             "moe_silu_mul_quant": (I32, [D, I32, P, P, P, P, P]),
             "moe_grouped_gemm2_workspace": (I32, [D, I32, ctypes.POINTER(SZ)]),
             "moe_grouped_gemm2": (I32, [D, I32] + [P] * 8 + [P, SZ, P]),
+            "moe_silu_mul_quant_mx": (I32, [D, I32, P, P, P, P, P]),
+            "moe_grouped_gemm2_mx": (I32, [D, I32] + [P] * 8 + [P, SZ, P]),
             "moe_combine": (I32, [D, I32, P, I64, P, P, P, P]),
         }
         for name, (res, args) in sig.items():
@@ -245,6 +248,32 @@ def moe_grouped_gemm2(d: Dims, inter: int, h_e4m3, h_scale, expert_offsets, row_
     _check("moe_grouped_gemm2", st)
 
 
+def moe_silu_mul_quant_mx(d: Dims, inter: int, y1_bf16, totals, h_e4m3, h_scale) -> None:
+    rows_cap = d.T * d.k
+    st = lib().moe_silu_mul_quant_mx(
+        ctypes.byref(d.c()), inter, _ptr(y1_bf16, "y1_bf16", 2 * rows_cap * 2 * inter, 2),
+        _i32(totals, "totals", 2), _ptr(h_e4m3, "h_e4m3", rows_cap * inter, 1),
+        _u32(h_scale, "h_scale", rows_cap * (inter // 128)), _stream())
+    _check("moe_silu_mul_quant_mx", st)
+
+
+def moe_grouped_gemm2_mx(d: Dims, inter: int, h_e4m3, h_scale, expert_offsets, row_assign, topk_w,
+                         w2_e4m3, w2_scale, y2_bf16, ws=None) -> None:
+    T, H, L = d.T, d.H, d.L
+    rows_cap = T * d.k
+    if topk_w is not None and topk_w.dtype != torch.float32:
+        raise ValueError("topk_w must be float32")
+    st = lib().moe_grouped_gemm2_mx(
+        ctypes.byref(d.c()), inter, _ptr(h_e4m3, "h_e4m3", rows_cap * inter, 1),
+        _u32(h_scale, "h_scale", rows_cap * (inter // 128)),
+        _i32(expert_offsets, "expert_offsets", L + 1), _i32(row_assign, "row_assign", rows_cap),
+        _ptr(topk_w, "topk_w", 4 * T * d.k, 4), _ptr(w2_e4m3, "w2_e4m3", L * H * inter, 1),
+        _u32(w2_scale, "w2_scale", L * (inter // 128) * H),
+        _ptr(y2_bf16, "y2_bf16", 2 * rows_cap * H, 2), _ptr(ws, "ws", moe_grouped_gemm2_workspace(d, inter)),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream())
+    _check("moe_grouped_gemm2_mx", st)
+
+
 def moe_combine(d: Dims, width: int, y_bf16, assign_row, topk_w, out_bf16) -> None:
     T, k = d.T, d.k
     y_rows = 0 if y_bf16 is None else y_bf16.numel() // max(width, 1)
@@ -333,6 +362,23 @@ def grouped_gemm2(d: Dims, inter: int, h, h_scale, lay: dict, topk_w, w2_e4m3, w
     ws = alloc_gemm2_workspace(d, inter, h.device) if ws is None else ws
     moe_grouped_gemm2(d, inter, h, h_scale, lay["expert_offsets"], lay["row_assign"], topk_w, w2_e4m3, w2_scale,
                       y2, ws)
+    return y2
+
+
+def silu_mul_quant_mx(d: Dims, inter: int, y1, lay: dict, h=None, h_scale=None):
+    rows = max(d.T * d.k, 1)
+    h = torch.empty((rows, inter), dtype=torch.uint8, device=y1.device) if h is None else h
+    h_scale = (torch.empty((rows, inter // 128), dtype=torch.int32, device=y1.device)
+               if h_scale is None else h_scale)
+    moe_silu_mul_quant_mx(d, inter, y1, lay["totals"], h, h_scale)
+    return h, h_scale
+
+
+def grouped_gemm2_mx(d: Dims, inter: int, h, h_scale, lay: dict, topk_w, w2_e4m3, w2_scale, y2=None, ws=None):
+    y2 = torch.empty((max(d.T * d.k, 1), d.H), dtype=torch.bfloat16, device=h.device) if y2 is None else y2
+    ws = alloc_gemm2_workspace(d, inter, h.device) if ws is None else ws
+    moe_grouped_gemm2_mx(d, inter, h, h_scale, lay["expert_offsets"], lay["row_assign"], topk_w, w2_e4m3,
+                         w2_scale, y2, ws)
     return y2
 
 

@@ -79,4 +79,22 @@ __device__ __forceinline__ float encode_block16(const float (&xv)[16], float ama
     return zero ? 0.0f : s;
 }
 
+// MX (e8m0) group exponent: E = ceil(log2(t)), t = amax / 448 (IEEE fp32
+// division), read off t's bits (an exact power of two keeps its exponent,
+// anything above it rounds up), clamped to [-127, 127]; an all-zero group
+// (amax == 0) gives -127.  For finite amax, E <= 120, so 2^-E is a normal float.
+__device__ __forceinline__ int mx_exponent(float amax) {
+    if (!(amax > 0.0f)) return -127;
+    const uint32_t b = __float_as_uint(amax / 448.0f);
+    const int ex = (int)((b >> 23) & 0xFF);
+    const uint32_t man = b & 0x7FFFFFu;
+    int E;
+    if (ex == 0) E = man > 0x400000u ? -126 : -127;     // subnormal t: (2^-127, 2^-126) or below
+    else E = ex - 127 + (man != 0 ? 1 : 0);
+    return max(-127, min(127, E));
+}
+
+// 2^-E as a float (E in [-127, 120])
+__device__ __forceinline__ float exp2_neg(int E) { return __uint_as_float((uint32_t)(127 - E) << 23); }
+
 }  // namespace moe

@@ -110,13 +110,17 @@ struct Cfg {
 // accumulate in the MFMA itself and there is no fold.
 // DIRECT: the A operand's rows are the expert-major rows themselves (row r of
 // the tile reads A row r; GEMM2 on stage2's output), instead of rows gathered
-// through the rowmap; T is then the number of A rows.
+// through the rowmap; T is then the number of A rows.  MX && DIRECT (the MX
+// GEMM2): each output row is multiplied by wtab[row] (its routing weight)
+// before the bf16 rounding; a weight that is not a power of two cannot ride in
+// the e8m0 codes.
 template <class C, bool MX, bool DIRECT>
 __global__ void __launch_bounds__(C::kThreads, 1)
 grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__ row_scale,
                      const int4* __restrict__ tiles, const int32_t* __restrict__ row_slot,
                      const uint8_t* __restrict__ w, const void* __restrict__ w_scale_v,
-                     uint16_t* __restrict__ y, int N, int H, int64_t T, int64_t scale_ld) {
+                     uint16_t* __restrict__ y, int N, int H, int64_t T, int64_t scale_ld,
+                     const float* __restrict__ wtab) {
     // fp32 path: one float per (expert, 128 columns, K block), [L, N/128, H/128];
     // MX path: packed e8m0 codes per (expert, K block, column), [L, H/128, N]
     const float* w_scale = static_cast<const float*>(w_scale_v);
@@ -256,6 +260,12 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
         for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < NJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        // MX GEMM2: the rows' routing weights, loaded now and used by the epilogue
+        float wr[MI];
+        if constexpr (MX && DIRECT) {
+#pragma unroll
+            for (int i = 0; i < MI; ++i) wr[i] = wtab[r0 + min(wm * RW + i * 16 + (lane & 15), nvalid - 1)];
+        }
 
         for (int kb = 0; kb < KB; ++kb, ++g) {
             cbarrier();
@@ -397,6 +407,10 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
             for (int i = 0; i < MI; ++i) {
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
+                    if constexpr (MX && DIRECT) {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) acc[i][j][v] *= wr[i];
+                    }
                     const uint32_t lo = moe::f32_to_bf16_rne(acc[i][j][0]) | (moe::f32_to_bf16_rne(acc[i][j][1]) << 16);
                     const uint32_t hi = moe::f32_to_bf16_rne(acc[i][j][2]) | (moe::f32_to_bf16_rne(acc[i][j][3]) << 16);
                     // columns j*16 + 4q .. +3 = byte 32j + 8q of the 128 B row: chunk 2j + q/2
@@ -427,6 +441,8 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
 //    consecutive threads write consecutive words.  A row id outside [0, T)
 //    gets the word 0 (fp32 scale 0: a zero row; e8m0 codes 0: the scale
 //    2^-127 on slot 0's payload), as does a weight index outside [0, n_assign).
+//    With e8m0 codes the weights are not folded in (wtab non-null): row r's
+//    weight goes to wtab[r] for the main kernel's epilogue.
 //  * tile descriptors (the last workgroup): per local expert ceil(count / BM)
 //    row tiles times NT column tiles, experts in order, column tiles outer and
 //    row tiles inner; tiles[0].x = number of tiles, tiles[1 + t] =
@@ -435,6 +451,7 @@ template <int BM>
 __global__ void __launch_bounds__(256)
 gemm1_prep_kernel(const uint32_t* __restrict__ q_scale, const int32_t* __restrict__ row_slot,
                   const int32_t* __restrict__ row_assign, const float* __restrict__ topk_w, int64_t n_assign,
+                  float* __restrict__ wtab,
                   const int32_t* __restrict__ expert_offsets, int L, int KB, int NT, int64_t T,
                   int64_t rows_cap, int64_t scale_ld, uint32_t* __restrict__ out, int4* __restrict__ tiles,
                   int64_t tiles_cap) {
@@ -514,10 +531,11 @@ gemm1_prep_kernel(const uint32_t* __restrict__ q_scale, const int32_t* __restric
         uint32_t v[kPrepKb];
 #pragma unroll
         for (int i = 0; i < kPrepKb; ++i) v[i] = (ok && k0 + i < KB) ? src[k0 + i] : 0u;
-        if (topk_w) {
+        if (topk_w && !wtab) {
 #pragma unroll
             for (int i = 0; i < kPrepKb; ++i) v[i] = __float_as_uint(__uint_as_float(v[i]) * wr);
         }
+        if (wtab && kg == 0) wtab[r] = wr;
 #pragma unroll
         for (int i = 0; i < kPrepKb; ++i)
             if (k0 + i < KB) out[(int64_t)(k0 + i) * scale_ld + r] = v[i];
@@ -544,15 +562,17 @@ static_assert(TileCfg::BM <= kMaxBM, "scale table padding covers one tile");
 
 // Workspace: the row-scale table, then the tile descriptors (16 B each).
 struct WsLayout {
-    int64_t scale_ld, table_bytes, tiles_cap, bytes;
+    int64_t scale_ld, table_bytes, tiles_cap, wtab_off, bytes;
 };
-// rows_cap expert-major rows, KB K blocks, n output columns, L experts
-WsLayout ws_layout(int64_t rows_cap, int64_t KB, int64_t n, int64_t L) {
+// rows_cap expert-major rows, KB K blocks, n output columns, L experts; with
+// row weights (GEMM2), a float per row after the descriptors (256 B aligned)
+WsLayout ws_layout(int64_t rows_cap, int64_t KB, int64_t n, int64_t L, bool row_weights) {
     WsLayout l;
     l.scale_ld = scale_ld_of(rows_cap);
     l.table_bytes = (KB * l.scale_ld * 4 + 255) & ~int64_t(255);
     l.tiles_cap = (rows_cap / kMinBM + L) * ((n + BN - 1) / BN);
-    l.bytes = l.table_bytes + (1 + l.tiles_cap) * 16;
+    l.wtab_off = (l.table_bytes + (1 + l.tiles_cap) * 16 + 255) & ~int64_t(255);
+    l.bytes = row_weights ? l.wtab_off + rows_cap * 4 : l.table_bytes + (1 + l.tiles_cap) * 16;
     return l;
 }
 
@@ -566,7 +586,6 @@ moe_status run_gemm(const moe::Dims& d, int64_t a_rows, int64_t kdim, int64_t n,
                     const uint32_t* q_scale, const int32_t* row_slot, const int32_t* row_assign,
                     const float* topk_w, const int32_t* expert_offsets, const uint8_t* w_e4m3,
                     const void* w_scale, uint16_t* y_bf16, void* ws, size_t ws_bytes, void* hip_stream) {
-    static_assert(!(MX && DIRECT), "no MX GEMM2");
     if (n < 128 || n % 128 != 0 || kdim < 128 || kdim % 128 != 0) return MOE_ERR_INVALID_ARG;
     if (d.L > kMaxL) return MOE_ERR_UNSUPPORTED;
     if (d.T == 0) return MOE_OK;
@@ -580,7 +599,7 @@ moe_status run_gemm(const moe::Dims& d, int64_t a_rows, int64_t kdim, int64_t n,
         rows_cap * n >= ((int64_t)1 << 40) || rows_cap / kMinBM >= ((int64_t)1 << 22))
         return MOE_ERR_UNSUPPORTED;
     const int64_t KB = kdim / BK;
-    const WsLayout wl = ws_layout(rows_cap, KB, n, d.L);
+    const WsLayout wl = ws_layout(rows_cap, KB, n, d.L, DIRECT);
     if (!ws || ws_bytes < (size_t)wl.bytes) return MOE_ERR_WORKSPACE;
     if (KB * wl.scale_ld >= ((int64_t)1 << 31) || wl.tiles_cap >= ((int64_t)1 << 31) - 1)
         return MOE_ERR_UNSUPPORTED;
@@ -589,19 +608,21 @@ moe_status run_gemm(const moe::Dims& d, int64_t a_rows, int64_t kdim, int64_t n,
     hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
     uint32_t* row_scale = reinterpret_cast<uint32_t*>(ws);
     int4* tiles = reinterpret_cast<int4*>(static_cast<uint8_t*>(ws) + wl.table_bytes);
+    // MX GEMM2's per-row weights (the fp32 path folds them into the row scales)
+    float* wtab = (MX && DIRECT) ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + wl.wtab_off) : nullptr;
     const int NT = (int)((n + BN - 1) / BN);
     // gather workgroups plus the planning workgroup (the last one)
     const int64_t KG = (KB + kPrepKb - 1) / kPrepKb;
     const int pgrid = (int)std::min<int64_t>((rows_cap * KG + 255) / 256, 4096) + 1;
     hipLaunchKernelGGL((gemm1_prep_kernel<TileCfg::BM>), dim3(pgrid), dim3(256), 0, stream, q_scale,
-                       DIRECT ? nullptr : row_slot, row_assign, topk_w, rows_cap, expert_offsets, (int)d.L,
+                       DIRECT ? nullptr : row_slot, row_assign, topk_w, rows_cap, wtab, expert_offsets, (int)d.L,
                        (int)KB, NT, a_rows, rows_cap, wl.scale_ld, row_scale, tiles, wl.tiles_cap);
     moe_status st;
     if ((st = moe::launch_status()) != MOE_OK) return st;
     const int grid = ((cus + kXcds - 1) / kXcds) * kXcds;
     hipLaunchKernelGGL((grouped_gemm1_kernel<TileCfg, MX, DIRECT>), dim3(grid), dim3(TileCfg::kThreads), 0,
                        stream, q_e4m3, row_scale, tiles, row_slot, w_e4m3, w_scale, y_bf16, (int)n, (int)kdim,
-                       a_rows, wl.scale_ld);
+                       a_rows, wl.scale_ld, wtab);
     return moe::launch_status();
 }
 
@@ -614,7 +635,7 @@ extern "C" moe_status moe_grouped_gemm1_workspace(const moe_dims* dims, int32_t 
     moe_status st = load(dims, &d);
     if (st != MOE_OK) return st;
     if (!bytes || n < 128 || n % 128 != 0) return MOE_ERR_INVALID_ARG;
-    *bytes = (size_t)ws_layout(d.T * d.k, d.H / BK, n, d.L).bytes;
+    *bytes = (size_t)ws_layout(d.T * d.k, d.H / BK, n, d.L, false).bytes;
     return MOE_OK;
 }
 
@@ -649,7 +670,7 @@ extern "C" moe_status moe_grouped_gemm2_workspace(const moe_dims* dims, int32_t 
     moe_status st = load(dims, &d);
     if (st != MOE_OK) return st;
     if (!bytes || inter < 128 || inter % 128 != 0) return MOE_ERR_INVALID_ARG;
-    *bytes = (size_t)ws_layout(d.T * d.k, inter / BK, d.H, d.L).bytes;
+    *bytes = (size_t)ws_layout(d.T * d.k, inter / BK, d.H, d.L, true).bytes;
     return MOE_OK;
 }
 
@@ -665,4 +686,17 @@ extern "C" moe_status moe_grouped_gemm2(const moe_dims* dims, int32_t inter, con
     return run_gemm<false, true>(d, d.T * d.k, inter, d.H, h_e4m3, reinterpret_cast<const uint32_t*>(h_scale),
                                  nullptr, row_assign, topk_w, expert_offsets, w2_e4m3, w2_scale, y2_bf16, ws,
                                  ws_bytes, hip_stream);
+}
+
+extern "C" moe_status moe_grouped_gemm2_mx(const moe_dims* dims, int32_t inter, const uint8_t* h_e4m3,
+                                           const uint32_t* h_scale, const int32_t* expert_offsets,
+                                           const int32_t* row_assign, const float* topk_w,
+                                           const uint8_t* w2_e4m3, const uint32_t* w2_scale, uint16_t* y2_bf16,
+                                           void* ws, size_t ws_bytes, void* hip_stream) {
+    moe::Dims d;
+    moe_status st = load(dims, &d);
+    if (st != MOE_OK) return st;
+    if (d.T != 0 && (!row_assign || !topk_w)) return MOE_ERR_INVALID_ARG;
+    return run_gemm<true, true>(d, d.T * d.k, inter, d.H, h_e4m3, h_scale, nullptr, row_assign, topk_w,
+                                expert_offsets, w2_e4m3, w2_scale, y2_bf16, ws, ws_bytes, hip_stream);
 }

@@ -96,24 +96,12 @@ quant_dispatch_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict_
 // MX-style variant ("Where we stand": e8m0 block scales; commit
 // "ready-first / quant-lds-store": packed four per dword): groups of 32
 // elements, a group being one lane pair of the mapping above.  Per group:
-// t = amax / 448 (IEEE fp32), E = ceil(log2 t) read off t's bits (an exact
-// power of two keeps its exponent, anything above it rounds up), clamped to
-// [-127, 127] (an all-zero group: -127); payload = e4m3(x * 2^-E), the scaling
+// E = moe::mx_exponent(amax) (ceil(log2(amax / 448)), clamped; an all-zero
+// group: -127); payload = e4m3(x * 2^-E), the scaling
 // exact, so the hardware conversion's round to nearest even is the only
 // rounding and no magnitude exceeds 448 (an all-zero group: zero bytes);
 // code = E + 127, the four codes of a 128-element block packed into one dword
 // (group g of the block in byte g).
-__device__ __forceinline__ int ceil_log2_over_448(uint32_t amax_bits16) {
-    if (amax_bits16 == 0) return -127;
-    const float t = __uint_as_float(amax_bits16 << 16) / 448.0f;
-    const uint32_t b = __float_as_uint(t);
-    const int ex = (int)((b >> 23) & 0xFF);
-    const uint32_t man = b & 0x7FFFFFu;
-    int E;
-    if (ex == 0) E = man > 0x400000u ? -126 : -127;     // subnormal t: (2^-127, 2^-126) or below
-    else E = ex - 127 + (man != 0 ? 1 : 0);
-    return max(-127, min(127, E));
-}
 
 __global__ void __launch_bounds__(kBlock)
 quant_dispatch_mx_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ slot_tok,
@@ -156,8 +144,8 @@ quant_dispatch_mx_kernel(const uint16_t* __restrict__ x, const int32_t* __restri
             }
             uint32_t m = max((uint32_t)m2.x, (uint32_t)m2.y);
             m = max(m, dpp<0xB1>(m));                     // the lane pair = one group of 32
-            const int E = ceil_log2_over_448(m);
-            const float p2 = __uint_as_float((uint32_t)(127 - E) << 23);   // 2^-E, E <= 120 for bf16
+            const int E = moe::mx_exponent(__uint_as_float(m << 16));
+            const float p2 = moe::exp2_neg(E);
             // an all-zero group (negative zeros included) stores zero bytes
             const bool zero = m == 0;
             uint32_t out[4];

@@ -14,6 +14,12 @@
 // lanes by DPP, the block's codes and scale by encode_block16 (exact given
 // h), and one contiguous 16 B code store per lane.  HBM bound: per row it
 // reads 4I bytes and writes I + I/32.
+//
+// MX variant (the pages' e8m0 format, "Where we stand"; packed four per dword,
+// commit "ready-first / quant-lds-store"): a group of 32 elements of h is one
+// lane pair, its |max| one DPP exchange, E = mx_exponent(|max|), payload
+// e4m3(h * 2^-E) (exact scaling), the block's four codes packed by lane
+// shuffles into one dword per 128 elements.
 #include "fp8_block.h"
 
 namespace {
@@ -27,9 +33,10 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
     return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
+template <bool MX>
 __global__ void __launch_bounds__(kBlock)
 silu_mul_quant_kernel(const uint16_t* __restrict__ y1, const int32_t* __restrict__ totals, int64_t rows_cap,
-                      int I, uint8_t* __restrict__ q, float* __restrict__ q_scale) {
+                      int I, uint8_t* __restrict__ q, void* __restrict__ q_scale_v) {
     const int64_t R = min((int64_t)totals[0], rows_cap);
     const int lane = threadIdx.x % MOE_WAVE;
     const int sub = lane & 7;
@@ -56,22 +63,41 @@ silu_mul_quant_kernel(const uint16_t* __restrict__ y1, const int32_t* __restrict
             m = max(m, __float_as_uint(h[2 * i]) & 0x7FFFFFFFu);
             m = max(m, __float_as_uint(h[2 * i + 1]) & 0x7FFFFFFFu);
         }
-        m = moe::group8_max(m);
         uint32_t out[4];
-        const float s = moe::encode_block16(h, __uint_as_float(m), out);
-        if (act) {
-            moe::u32x4* dst = reinterpret_cast<moe::u32x4*>(q + r * I + b * 128 + sub * 16);
-            __builtin_nontemporal_store(moe::u32x4{out[0], out[1], out[2], out[3]}, dst);
-            if (sub == 0) q_scale[r * nblk + b] = s;
+        moe::u32x4* dst = reinterpret_cast<moe::u32x4*>(q + r * I + b * 128 + sub * 16);
+        if constexpr (MX) {
+            m = max(m, moe::dpp<0xB1>(m));                  // the lane pair = one group of 32
+            const int E = moe::mx_exponent(__uint_as_float(m));
+            const float p2 = moe::exp2_neg(E);
+            const bool zero = m == 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                out[i] = zero ? 0u : moe::cvt4(h[4 * i] * p2, h[4 * i + 1] * p2, h[4 * i + 2] * p2, h[4 * i + 3] * p2);
+            // codes of the block's groups 0..3 sit in lanes sub = 0, 2, 4, 6
+            const int code = E + 127;
+            const int base = lane & ~7;
+            const uint32_t packed = (uint32_t)__shfl(code, base, MOE_WAVE) |
+                                    ((uint32_t)__shfl(code, base + 2, MOE_WAVE) << 8) |
+                                    ((uint32_t)__shfl(code, base + 4, MOE_WAVE) << 16) |
+                                    ((uint32_t)__shfl(code, base + 6, MOE_WAVE) << 24);
+            if (act) {
+                __builtin_nontemporal_store(moe::u32x4{out[0], out[1], out[2], out[3]}, dst);
+                if (sub == 0) static_cast<uint32_t*>(q_scale_v)[r * nblk + b] = packed;
+            }
+        } else {
+            m = moe::group8_max(m);
+            const float s = moe::encode_block16(h, __uint_as_float(m), out);
+            if (act) {
+                __builtin_nontemporal_store(moe::u32x4{out[0], out[1], out[2], out[3]}, dst);
+                if (sub == 0) static_cast<float*>(q_scale_v)[r * nblk + b] = s;
+            }
         }
     }
 }
 
-}  // namespace
-
-extern "C" moe_status moe_silu_mul_quant(const moe_dims* dims, int32_t inter, const uint16_t* y1_bf16,
-                                         const int32_t* totals, uint8_t* h_e4m3, float* h_scale,
-                                         void* hip_stream) {
+template <bool MX>
+moe_status run_silu_mul_quant(const moe_dims* dims, int32_t inter, const uint16_t* y1_bf16, const int32_t* totals,
+                              uint8_t* h_e4m3, void* h_scale, void* hip_stream) {
     moe::Dims d;
     moe_status st = moe::load_dims(dims, &d, false);
     if (st != MOE_OK) return st;
@@ -82,8 +108,22 @@ extern "C" moe_status moe_silu_mul_quant(const moe_dims* dims, int32_t inter, co
     if (rows_cap * 2 * inter >= ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
     const int64_t items = rows_cap * ((inter / 128 + 7) / 8);
     const int grid = (int)std::min<int64_t>((items + kWaves - 1) / kWaves, 16384);
-    hipLaunchKernelGGL(silu_mul_quant_kernel, dim3(grid), dim3(kBlock), 0,
+    hipLaunchKernelGGL(silu_mul_quant_kernel<MX>, dim3(grid), dim3(kBlock), 0,
                        reinterpret_cast<hipStream_t>(hip_stream), y1_bf16, totals, rows_cap, (int)inter,
                        h_e4m3, h_scale);
     return moe::launch_status();
+}
+
+}  // namespace
+
+extern "C" moe_status moe_silu_mul_quant(const moe_dims* dims, int32_t inter, const uint16_t* y1_bf16,
+                                         const int32_t* totals, uint8_t* h_e4m3, float* h_scale,
+                                         void* hip_stream) {
+    return run_silu_mul_quant<false>(dims, inter, y1_bf16, totals, h_e4m3, h_scale, hip_stream);
+}
+
+extern "C" moe_status moe_silu_mul_quant_mx(const moe_dims* dims, int32_t inter, const uint16_t* y1_bf16,
+                                            const int32_t* totals, uint8_t* h_e4m3, uint32_t* h_scale,
+                                            void* hip_stream) {
+    return run_silu_mul_quant<true>(dims, inter, y1_bf16, totals, h_e4m3, h_scale, hip_stream);
 }

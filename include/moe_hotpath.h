@@ -239,9 +239,10 @@ moe_status moe_silu_mul_quant(const moe_dims* dims, int32_t inter, const uint16_
                               const int32_t* totals, uint8_t* h_e4m3, float* h_scale,
                               void* hip_stream);
 
-/* Workspace bytes moe_grouped_gemm2 needs (host-only): the K-block-major row
- * scale table, (inter/128) x (rows_cap + 256, rounded up to 64) floats (padded
- * to 256 B), then (1 + (rows_cap/128 + L) * ceil(H/256)) 16 B tile descriptors. */
+/* Workspace bytes moe_grouped_gemm2 and moe_grouped_gemm2_mx need (host-only):
+ * the K-block-major row scale table, (inter/128) x (rows_cap + 256, rounded up
+ * to 64) words (padded to 256 B), then (1 + (rows_cap/128 + L) * ceil(H/256))
+ * 16 B tile descriptors, then (from a 256 B boundary) one float per row. */
 moe_status moe_grouped_gemm2_workspace(const moe_dims* dims, int32_t inter, size_t* bytes);
 
 /*
@@ -270,6 +271,34 @@ moe_status moe_grouped_gemm2(const moe_dims* dims, int32_t inter,
                              const float* topk_w,
                              const uint8_t* w2_e4m3, const float* w2_scale,
                              uint16_t* y2_bf16, void* ws, size_t ws_bytes, void* hip_stream);
+
+/*
+ * MX variants of stage2 (the pages' e8m0 format, as moe_quant_dispatch_mx and
+ * moe_grouped_gemm1_mx):
+ *
+ * moe_silu_mul_quant_mx: h as in moe_silu_mul_quant, quantised per group of
+ * 32 elements: E = ceil(log2(max|h| / 448)) exactly from the fp32 quotient
+ * (clamped to [-127, 127]; an all-zero group -127 with zero bytes), payload
+ * e4m3(h * 2^-E); the codes E + 127 of a 128-element block packed into one
+ * uint32 (group g of the block in byte g).
+ * Out: h_e4m3 uint8 [rows_cap, inter]; h_scale uint32 [rows_cap, inter/128].
+ *
+ * moe_grouped_gemm2_mx: y2 as in moe_grouped_gemm2 with e8m0 group scales on
+ * both operands (w2_scale uint32 [L, inter/128, H]: the packed codes of column
+ * c's groups 4kb .. 4kb+3 at [le, kb, c]); the routing weight w_r multiplies
+ * the fp32 sum before the bf16 rounding (it is not a power of two, so it
+ * cannot ride in the codes).  ws: moe_grouped_gemm2_workspace bytes.
+ */
+moe_status moe_silu_mul_quant_mx(const moe_dims* dims, int32_t inter, const uint16_t* y1_bf16,
+                                 const int32_t* totals, uint8_t* h_e4m3, uint32_t* h_scale,
+                                 void* hip_stream);
+
+moe_status moe_grouped_gemm2_mx(const moe_dims* dims, int32_t inter,
+                                const uint8_t* h_e4m3, const uint32_t* h_scale,
+                                const int32_t* expert_offsets, const int32_t* row_assign,
+                                const float* topk_w,
+                                const uint8_t* w2_e4m3, const uint32_t* w2_scale,
+                                uint16_t* y2_bf16, void* ws, size_t ws_bytes, void* hip_stream);
 
 /*
  * Step 4: combine.  Top-k weighted gather-sum back to token order (TilePipe:

@@ -116,7 +116,9 @@ def test_stage2_and_mx_workspaces(L):
     # GEMM2: K = inter, n = H; the same table + descriptor layout as GEMM1's
     inter = 2048
     table = ((inter // 128) * ((16384 * 8 + 256 + 63) // 64 * 64) * 4 + 255) // 256 * 256
-    assert b.moe_grouped_gemm2_workspace(d, inter) == table + (1 + (16384 * 8 // 128 + 32) * (7168 // 256)) * 16
+    desc_end = table + (1 + (16384 * 8 // 128 + 32) * (7168 // 256)) * 16
+    # then one float per row, from a 256 B boundary
+    assert b.moe_grouped_gemm2_workspace(d, inter) == (desc_end + 255) // 256 * 256 + 16384 * 8 * 4
     for bad in (0, 64, 200):
         with pytest.raises(b.MoeError):
             b.moe_grouped_gemm2_workspace(d, bad)
@@ -136,6 +138,9 @@ def test_stage2_and_mx_validation_before_any_launch(L):
     assert L.moe_grouped_gemm2(ctypes.byref(d), 128, *args, fake, 1 << 30, None) == -1
     # a short workspace
     assert L.moe_grouped_gemm2(ctypes.byref(d), 128, *([fake] * 8), fake, 16, None) == -2
+    assert L.moe_grouped_gemm2_mx(ctypes.byref(d), 128, *args, fake, 1 << 30, None) == -1
+    assert L.moe_grouped_gemm2_mx(ctypes.byref(d), 128, *([fake] * 8), fake, 16, None) == -2
+    assert L.moe_silu_mul_quant_mx(ctypes.byref(d), 100, fake, fake, fake, fake, None) == -1
 
 
 def test_stage2_and_mx_empty_input_calls_are_noops(L):
@@ -145,3 +150,5 @@ def test_stage2_and_mx_empty_input_calls_are_noops(L):
     assert L.moe_grouped_gemm1_mx(ctypes.byref(d), 256, *([None] * 7), None, 0, None) == 0
     assert L.moe_silu_mul_quant(ctypes.byref(d), 128, None, None, None, None, None) == 0
     assert L.moe_grouped_gemm2(ctypes.byref(d), 128, *([None] * 8), None, 0, None) == 0
+    assert L.moe_silu_mul_quant_mx(ctypes.byref(d), 128, None, None, None, None, None) == 0
+    assert L.moe_grouped_gemm2_mx(ctypes.byref(d), 128, *([None] * 8), None, 0, None) == 0
