@@ -17,7 +17,8 @@ in a separate A/B loop that alternates one fp32-scale stage1 step with one MX
 step (the clock drifts over a run, so only interleaved numbers compare), and
 reported under "mx".  Stage2 on GEMM1's output (silu(gate) * up with its fp8
 quant -> grouped GEMM2 with the routing weights -> combine of the local rows)
-is timed after that and reported under "stage2".
+is timed after that and reported under "stage2", with its MX variant timed
+against it in an A/B loop of the same kind under "stage2.mx".
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--no-cpu-baseline] [--copy-calib]
@@ -99,7 +100,9 @@ def algorithmic(w, R, U, Rc):
     combine_local = R * H * 2 + T * k * 8 + T * H * 2
     return dict(layout_local=lay_local, quant=quant, gemm1_flop=gemm_flop, gemm1_bytes=gemm_bytes,
                 layout_full=lay_full, combine=combine, quant_mx=quant, gemm1_mx_bytes=gemm_mx_bytes,
-                silu_mul_quant=act, gemm2_flop=gemm2_flop, gemm2_bytes=gemm2_bytes, combine_local=combine_local)
+                silu_mul_quant=act, gemm2_flop=gemm2_flop, gemm2_bytes=gemm2_bytes, combine_local=combine_local,
+                silu_mul_quant_mx=act,
+                gemm2_mx_bytes=R * (I + I // 32) + L * H * I + L * (I // 128) * H * 4 + R * 8 + R * H * 2)
 
 
 def main():
@@ -365,7 +368,54 @@ def stage2(torch, moe, w, d, lay, y1, wts_d, alg, traffic, args):
                 "frac": round(a / HBM_PEAK_GBS, 4), "traffic": traffic.get(n), "algorithmic_bytes": int(alg[key])}
 
     ga = alg["gemm2_flop"] / (med["gemm2"] * 1e-6) / 1e12
-    del w2_d, w2s_d, h, hs, y2, out
+
+    # MX variant, A/B against the fp32-scale stage2 on the same GEMM1 output
+    t0 = time.time()
+    m2, m2s = workloads.weights2_mx(w)
+    log(f"[bench] MX GEMM2 weights generated in {time.time() - t0:.1f}s")
+    m2_d, m2s_d = torch.from_numpy(m2).cuda(), torch.from_numpy(m2s.view(np.int32)).cuda()
+    del m2, m2s
+    hm = torch.empty((rows_cap, I), dtype=torch.uint8, device="cuda")
+    hms = torch.empty((rows_cap, I // 128), dtype=torch.int32, device="cuda")
+    mx_names = ["silu_mul_quant_mx", "gemm2_mx", "combine_local"]
+
+    def step_mx(ev=None):
+        if ev: ev[0].record(stream)
+        moe.silu_mul_quant_mx(d, I, y1, lay, hm, hms)
+        if ev: ev[1].record(stream)
+        moe.grouped_gemm2_mx(d, I, hm, hms, lay, wts_d, m2_d, m2s_d, y2, g2_ws)
+        if ev: ev[2].record(stream)
+        moe.combine(d, w.H, y2, lay["assign_row"], ones, out)
+        if ev: ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step_mx()
+    evm = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(evf[i])
+        step_mx(evm[i])
+    torch.cuda.synchronize()
+    perm = {n: [e[j].elapsed_time(e[j + 1]) * 1e3 for e in evm] for j, n in enumerate(mx_names)}
+    medm = {n: float(np.median(v)) for n, v in perm.items()}
+    totm = [sum(perm[n][i] for n in mx_names) for i in range(args.steps)]
+    totf = [e[0].elapsed_time(e[3]) * 1e3 for e in evf]
+    gam = alg["gemm2_flop"] / (medm["gemm2_mx"] * 1e-6) / 1e12
+    qam = alg["silu_mul_quant_mx"] / (medm["silu_mul_quant_mx"] * 1e-6) / 1e9
+    del w2_d, w2s_d, m2_d, m2s_d, h, hs, hm, hms, y2, out
+    mx = {"us_median": round(float(np.median(totm)), 2),
+          "fp32_scale_us_same_loop": round(float(np.median(totf)), 2),
+          "mx_over_fp32": round(float(np.median(totm)) / float(np.median(totf)), 4),
+          "kernels_us_median": {n: round(medm[n], 2) for n in mx_names},
+          "kernels": {"silu_mul_quant_mx": {"bound": "hbm", "achieved": round(qam, 1), "peak": HBM_PEAK_GBS,
+                                            "unit": "GB/s", "frac": round(qam / HBM_PEAK_GBS, 4),
+                                            "traffic": traffic.get("silu_mul_quant_mx"),
+                                            "algorithmic_bytes": int(alg["silu_mul_quant_mx"])},
+                      "gemm2_mx": {"bound": "mfma", "achieved": round(gam, 1), "peak": FP8_PEAK_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": round(gam / FP8_PEAK_TFLOPS, 4),
+                                   "traffic": traffic.get("gemm2_mx"), "algorithmic_flop": int(alg["gemm2_flop"]),
+                                   "algorithmic_bytes": int(alg["gemm2_mx_bytes"])}}}
     return {"us_median": round(float(np.median(tot)), 2),
             "us_p10_p90": [round(float(np.percentile(tot, 10)), 2), round(float(np.percentile(tot, 90)), 2)],
             "inter": I, "kernels_us_median": {n: round(med[n], 2) for n in names},
@@ -374,7 +424,8 @@ def stage2(torch, moe, w, d, lay, y1, wts_d, alg, traffic, args):
                                   "unit": "TFLOP/s", "frac": round(ga / FP8_PEAK_TFLOPS, 4),
                                   "traffic": traffic.get("gemm2"), "algorithmic_flop": int(alg["gemm2_flop"]),
                                   "algorithmic_bytes": int(alg["gemm2_bytes"])},
-                        "combine_local": hbm("combine_local", "combine_local")}}
+                        "combine_local": hbm("combine_local", "combine_local")},
+            "mx": mx}
 
 
 def stage1_graph(torch, moe, d, ids_d, x_d, wq_d, ws_d, lay, q, qs, y1, g_ws, w, R, U, steps):
