@@ -2,7 +2,9 @@
 // the rowmap ("poc(cco): MegaMoE stage1 dispatch over SDMA", "What": GEMM1
 // reads its A rows in place through a rowmap; commit 1: fp8 rows and block
 // scales through the rowmap; "Where we stand": block-scaled fp8 tiles, one
-// expert per tile, the compute-bound loop of stage1).
+// expert per tile, the compute-bound loop of stage1).  The same kernel, by
+// template flags, is the MX variant (e8m0 group scales in the MFMA's
+// block-scale operands, MX) and stage2's GEMM2 (A rows read directly, DIRECT).
 //
 // y[r, c] = sum_kb (sum_{h in kb} qA[r,h] * qW[c,h]) * sA[r,kb] * sW[c/128,kb]
 //
@@ -12,7 +14,8 @@
 // K = 128), folded into the fp32 running sum by one FMA with sA[row] * sW.
 // The MFMA computes the transposed sub-tile (weight rows as its A operand), so
 // a lane holds 4 consecutive output columns of one row: one row scale per lane
-// and sub-tile row, and 8 contiguous output bytes per lane in the epilogue.
+// and sub-tile row; the epilogue regroups the bf16 outputs through LDS into
+// whole 128 B rows before storing them.
 //
 // Tile: 128 rows of one expert x 256 columns.  Workgroup of 12 wavefronts
 // (three per SIMD): 2 x 4 compute wavefronts of 64 x 64 outputs each, and 4
