@@ -79,6 +79,18 @@ constexpr int kPrepKb = 8;    // K blocks per row-scale gather work item
 // (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14)
 constexpr int wait_vm(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14); }
 
+// s_waitcnt vmcnt(n) for a wave-uniform n in [LO, HI] (the count is an
+// immediate of the instruction, so each value is its own instruction)
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vm_dyn(int n) {
+    if constexpr (LO == HI) {
+        __builtin_amdgcn_s_waitcnt(wait_vm(LO));
+    } else {
+        if (n == LO) __builtin_amdgcn_s_waitcnt(wait_vm(LO));
+        else wait_vm_dyn<LO + 1, HI>(n);
+    }
+}
+
 __device__ __forceinline__ void cbarrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -97,11 +109,14 @@ struct Cfg {
     static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
     static constexpr int S_BYTES = NLW * 256;                 // row scales of rows 0 .. 64 NLW - 1
     static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
-    static constexpr int A_LOADS = A_BYTES / (1024 * NLW), B_LOADS = B_BYTES / (1024 * NLW);
-    static constexpr int NLD = A_LOADS + B_LOADS + 1;         // loads per loader per stage
+    // A: BM/8 loads of 8 rows (1 KB); loader lw takes A_LO of them, one more if
+    // lw < A_EXTRA.  B: B_LOADS 1 KB loads each.
+    static constexpr int A_GROUPS = BM / 8, A_LO = A_GROUPS / NLW, A_EXTRA = A_GROUPS % NLW;
+    static constexpr int A_LOADS = A_LO + (A_EXTRA ? 1 : 0), B_LOADS = B_BYTES / (1024 * NLW);
+    static constexpr int NLD = A_LOADS + B_LOADS + 2;         // most loads a loader issues per stage
     static_assert(RW % 16 == 0 && CW % 16 == 0 && CW <= 128 && 128 % CW == 0, "wavefront tile");
-    static_assert(A_BYTES % (1024 * NLW) == 0 && B_BYTES % (1024 * NLW) == 0 && A_LOADS >= 1 &&
-                      B_LOADS >= 1, "equal whole 1 KB loads per loader");
+    static_assert(BM % 8 == 0 && B_BYTES % (1024 * NLW) == 0 && A_LO >= 1 && B_LOADS >= 1,
+                  "whole 1 KB loads");
     static_assert(NLW * 64 >= BM && BM >= kMinBM && kThreads <= 1024, "scale rows, descriptors, size");
     static_assert(NSTAGE >= 2 && NSTAGE <= 4 && NSTAGE * STAGE <= 160 * 1024 && 2 * NLD < 64, "ring");
     static_assert(LAG >= -1 && LAG <= 1, "fold placement");
@@ -134,11 +149,11 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
     constexpr int STAGE = C::STAGE + (MX ? C::NLW * 256 : 0);
     constexpr int A_LOADS = C::A_LOADS, B_LOADS = C::B_LOADS;
     // Per stage each loader issues its A and B loads plus at most one scale load:
-    // loaders lw < BM/64 bring rows lw*64 .. lw*64+63's scales (4 B a lane), and
+    // loaders lw < NSA bring rows lw*64 .. lw*64+63's scales (4 B a lane), and
     // in MX mode loader SB_LOADER brings the BN columns' scale dwords (16 B a lane)
-    constexpr int NSA = C::BM / 64, SB_LOADER = NSA;
-    constexpr int NLD = A_LOADS + B_LOADS + 1;
-    static_assert(C::BM % 64 == 0 && NSA <= C::NLW && (!MX || SB_LOADER < C::NLW), "scale loaders");
+    constexpr int NSA = (C::BM + 63) / 64, SB_LOADER = NSA;
+    constexpr int NLD = C::NLD;
+    static_assert(NSA <= C::NLW && (!MX || SB_LOADER < C::NLW), "scale loaders");
     static_assert(BN * 4 == 64 * 16, "one 16 B-a-lane load covers the column scales");
     static_assert(NSTAGE * STAGE <= 160 * 1024 && 2 * NLD < 64, "ring");
     __shared__ __align__(16) uint8_t ring[NSTAGE * STAGE];
@@ -158,6 +173,9 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
     if (wave >= C::kCompute) {
         // ---------------- loader wavefronts ----------------
         const int lw = wave - C::kCompute;
+        // this loader's A groups: a_cnt of them from a_start (wave-uniform)
+        const int a_cnt = C::A_LO + (lw < C::A_EXTRA ? 1 : 0);
+        const int a_start = lw * C::A_LO + min(lw, C::A_EXTRA);
         const int lrow = lane >> 3;
         const int gchunk = (lane & 7) ^ lrow;
         // 16 B chunk of the row's 128 K bytes that goes to logical chunk c: c itself,
@@ -186,14 +204,15 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
             // expert's last row reuse the first row's slot
             int sl[A_LOADS];
 #pragma unroll
-            for (int i = 0; i < A_LOADS; ++i)
-                sl[i] = DIRECT ? r0 + min((lw * A_LOADS + i) * 8 + lrow, nvalid - 1)
-                               : row_slot[r0 + min((lw * A_LOADS + i) * 8 + lrow, nvalid - 1)];
+            for (int i = 0; i < A_LOADS; ++i) {
+                const int rr = r0 + min((a_start + min(i, a_cnt - 1)) * 8 + lrow, nvalid - 1);
+                sl[i] = DIRECT ? rr : row_slot[rr];
+            }
 #pragma unroll
             for (int i = 0; i < A_LOADS; ++i) {
-                const int r = (lw * A_LOADS + i) * 8 + lrow;
+                const int r = (a_start + i) * 8 + lrow;
                 const int v = (r < nvalid && (uint64_t)sl[i] < (uint64_t)T) ? sl[i] : s0;
-                a_off[i] = (uint32_t)v * (uint32_t)H + kchunk(gchunk ^ ((lw * A_LOADS + i) & 1)) * 16;
+                a_off[i] = (uint32_t)v * (uint32_t)H + kchunk(gchunk ^ ((a_start + i) & 1)) * 16;
             }
             wexp = w + ((int64_t)e * N + n0) * H;
             srow = row_scale + r0 + lw * 64;
@@ -207,8 +226,9 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
             uint8_t* base = ring + (s % NSTAGE) * STAGE;
 #pragma unroll
             for (int i = 0; i < A_LOADS; ++i)
-                __builtin_amdgcn_global_load_lds(GPTR((q + kb * BK) + a_off[i]),
-                                                 LPTR(base + (lw * A_LOADS + i) * 1024), 16, 0, 0);
+                if (i < a_cnt)
+                    __builtin_amdgcn_global_load_lds(GPTR((q + kb * BK) + a_off[i]),
+                                                     LPTR(base + (a_start + i) * 1024), 16, 0, 0);
 #pragma unroll
             for (int i = 0; i < B_LOADS; ++i) {
                 // rows past a half tile re-read the first half (their columns are not stored)
@@ -226,20 +246,15 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
                                                  LPTR(base + A_BYTES + B_BYTES + C::NLW * 256), 16, 0, 0);
         };
         // loads this loader issues per stage (wave-uniform)
-        const bool full = lw < NSA || (MX && lw == SB_LOADER);
+        const int nld = a_cnt + B_LOADS + ((lw < NSA || (MX && lw == SB_LOADER)) ? 1 : 0);
+        constexpr int NLD_MIN = C::A_LO + B_LOADS;
         for (int s = 0; s < NSTAGE - 1 && s < nsteps; ++s) issue(s);
         for (int g = 0; g < nsteps; ++g) {
             // stage g has landed once at most the later stages' loads are outstanding
             const int later = min(NSTAGE - 2, nsteps - 1 - g);
-            if (full) {
-                if (later >= 2) __builtin_amdgcn_s_waitcnt(wait_vm(2 * NLD));
-                else if (later == 1) __builtin_amdgcn_s_waitcnt(wait_vm(NLD));
-                else __builtin_amdgcn_s_waitcnt(wait_vm(0));
-            } else {
-                if (later >= 2) __builtin_amdgcn_s_waitcnt(wait_vm(2 * (NLD - 1)));
-                else if (later == 1) __builtin_amdgcn_s_waitcnt(wait_vm(NLD - 1));
-                else __builtin_amdgcn_s_waitcnt(wait_vm(0));
-            }
+            if (later >= 2) wait_vm_dyn<2 * NLD_MIN, 2 * NLD>(2 * nld);
+            else if (later == 1) wait_vm_dyn<NLD_MIN, NLD>(nld);
+            else __builtin_amdgcn_s_waitcnt(wait_vm(0));
             cbarrier();
             if (g + NSTAGE - 1 < nsteps) issue(g + NSTAGE - 1);
         }
@@ -617,13 +632,14 @@ moe_status run_gemm(const moe::Dims& d, int64_t a_rows, int64_t kdim, int64_t n,
     // gather workgroups plus the planning workgroup (the last one)
     const int64_t KG = (KB + kPrepKb - 1) / kPrepKb;
     const int pgrid = (int)std::min<int64_t>((rows_cap * KG + 255) / 256, 4096) + 1;
-    hipLaunchKernelGGL((gemm1_prep_kernel<TileCfg::BM>), dim3(pgrid), dim3(256), 0, stream, q_scale,
+    using C = TileCfg;
+    hipLaunchKernelGGL((gemm1_prep_kernel<C::BM>), dim3(pgrid), dim3(256), 0, stream, q_scale,
                        DIRECT ? nullptr : row_slot, row_assign, topk_w, rows_cap, wtab, expert_offsets, (int)d.L,
                        (int)KB, NT, a_rows, rows_cap, wl.scale_ld, row_scale, tiles, wl.tiles_cap);
     moe_status st;
     if ((st = moe::launch_status()) != MOE_OK) return st;
     const int grid = ((cus + kXcds - 1) / kXcds) * kXcds;
-    hipLaunchKernelGGL((grouped_gemm1_kernel<TileCfg, MX, DIRECT>), dim3(grid), dim3(TileCfg::kThreads), 0,
+    hipLaunchKernelGGL((grouped_gemm1_kernel<C, MX, DIRECT>), dim3(grid), dim3(C::kThreads), 0,
                        stream, q_e4m3, row_scale, tiles, row_slot, w_e4m3, w_scale, y_bf16, (int)n, (int)kdim,
                        a_rows, wl.scale_ld, wtab);
     return moe::launch_status();
