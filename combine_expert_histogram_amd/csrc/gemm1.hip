@@ -47,7 +47,11 @@
 // scattered 4 B request per row and K block.  A pre-pass writes the scales
 // into a K-block-major table indexed by expert-major row (the caller's
 // workspace), and each loader brings 64 rows' scales per stage as one
-// contiguous 256 B piece.
+// contiguous 256 B piece.  The weights' scales of the stage's K block ride in
+// the same ring, so a step's operands and scales all come from LDS and the
+// compute wavefronts read them in the order of first use (column group 0 and
+// row group 0 first, the scales last: the fold that needs them comes one
+// column group later).
 //
 // Scheduling: one persistent workgroup per CU walks a tile table (experts in
 // order; per expert, column tiles outer and row tiles inner, so the row tiles
@@ -150,10 +154,12 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
     constexpr int A_LOADS = C::A_LOADS, B_LOADS = C::B_LOADS;
     // Per stage each loader issues its A and B loads plus at most one scale load:
     // loaders lw < NSA bring rows lw*64 .. lw*64+63's scales (4 B a lane), and
-    // in MX mode loader SB_LOADER brings the BN columns' scale dwords (16 B a lane)
+    // loader SB_LOADER brings the columns' scales: in MX mode the BN columns'
+    // dwords (16 B a lane, after the row scales' NLW * 256 bytes), else the two
+    // 128-column blocks' floats (lane l: block l & 1) at byte NSA * 256
     constexpr int NSA = (C::BM + 63) / 64, SB_LOADER = NSA;
     constexpr int NLD = C::NLD;
-    static_assert(NSA <= C::NLW && (!MX || SB_LOADER < C::NLW), "scale loaders");
+    static_assert(SB_LOADER < C::NLW && (NSA + 1) * 256 <= C::S_BYTES, "scale loaders");
     static_assert(BN * 4 == 64 * 16, "one 16 B-a-lane load covers the column scales");
     static_assert(NSTAGE * STAGE <= 160 * 1024 && 2 * NLD < 64, "ring");
     __shared__ __align__(16) uint8_t ring[NSTAGE * STAGE];
@@ -188,6 +194,7 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
         const uint32_t* srow = row_scale;
         int ncols = BN;
         const uint32_t* wsc_mx = w_scale_mx;
+        const float* wsc_f = w_scale;
         auto setup = [&](int it) __attribute__((always_inline)) {
             const int4 td = tiles[1 + it * G + my];
             const int e = td.x, r0 = td.z, nvalid = td.w & 511;
@@ -197,6 +204,8 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
                 // lane l: columns 4l .. 4l+3 (past a half tile: the last four again);
                 // N % 128 == 0 and n0 % 256 == 0 keep every address 16 B aligned
                 wsc_mx = w_scale_mx + (int64_t)e * KB * N + n0 + 4 * min(lane, ncols / 4 - 1);
+            } else {
+                wsc_f = w_scale + ((int64_t)e * NB + min(n0 / 128 + (lane & 1), NB - 1)) * KB;
             }
             int s0 = DIRECT ? r0 : row_slot[r0];
             if ((uint64_t)s0 >= (uint64_t)T) s0 = 0;
@@ -241,12 +250,17 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
             if (lw < NSA)
                 __builtin_amdgcn_global_load_lds(GPTR(reinterpret_cast<const uint8_t*>(srow + kb * scale_ld) + s_lane),
                                                  LPTR(base + A_BYTES + B_BYTES + lw * 256), 4, 0, 0);
-            else if (MX && lw == SB_LOADER)
-                __builtin_amdgcn_global_load_lds(GPTR(wsc_mx + (int64_t)kb * N),
-                                                 LPTR(base + A_BYTES + B_BYTES + C::NLW * 256), 16, 0, 0);
+            else if (lw == SB_LOADER) {
+                if (MX)
+                    __builtin_amdgcn_global_load_lds(GPTR(wsc_mx + (int64_t)kb * N),
+                                                     LPTR(base + A_BYTES + B_BYTES + C::NLW * 256), 16, 0, 0);
+                else
+                    __builtin_amdgcn_global_load_lds(GPTR(wsc_f + kb), LPTR(base + A_BYTES + B_BYTES + NSA * 256),
+                                                     4, 0, 0);
+            }
         };
         // loads this loader issues per stage (wave-uniform)
-        const int nld = a_cnt + B_LOADS + ((lw < NSA || (MX && lw == SB_LOADER)) ? 1 : 0);
+        const int nld = a_cnt + B_LOADS + ((lw < NSA || lw == SB_LOADER) ? 1 : 0);
         constexpr int NLD_MIN = C::A_LO + B_LOADS;
         for (int s = 0; s < NSTAGE - 1 && s < nsteps; ++s) issue(s);
         for (int g = 0; g < nsteps; ++g) {
@@ -271,7 +285,6 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
         const int n0 = td.y * BN;
         const int ncols = min(BN, N - n0);
         const bool active = wm * RW < nvalid && wn * CW < ncols;
-        const float* wsc = w_scale + ((int64_t)e * NB + min((n0 + wn * CW) / 128, NB - 1)) * KB;
 
         v4f acc[MI][NJ];
 #pragma unroll
@@ -339,19 +352,6 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
                 }
                 continue;
             }
-            const float sw = wsc[kb];
-            v8i af[MI];
-            float f[MI];
-#pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                const int row = wm * RW + i * 16 + (lane & 15);
-                const int c0 = (lane >> 4) * 2;
-                const int sw_r = (row & 7) ^ ((row >> 3) & 1);
-                const u32x4 a0 = *reinterpret_cast<const u32x4*>(As + row * BK + ((c0 ^ sw_r) << 4));
-                const u32x4 a1 = *reinterpret_cast<const u32x4*>(As + row * BK + (((c0 + 1) ^ sw_r) << 4));
-                af[i] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-                f[i] = Ss[row] * sw;
-            }
             // B fragment of column group j; group j+1's is read before group j's MFMAs
             auto read_b = [&](int j) __attribute__((always_inline)) {
                 const int col = wn * CW + j * 16 + (lane & 15);
@@ -361,8 +361,30 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
                 const u32x4 b1 = *reinterpret_cast<const u32x4*>(Bs + col * BK + (((c0 + 1) ^ sw_c) << 4));
                 return v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
             };
-            v4f pp[MI];
+            // reads in the order of first use: column group 0, the row groups, then the
+            // scales (first used by the folds of column group 0, one group later)
             v8i bnext = read_b(0);
+            __builtin_amdgcn_sched_barrier(0);
+            v8i af[MI];
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                const int row = wm * RW + i * 16 + (lane & 15);
+                const int c0 = (lane >> 4) * 2;
+                const int sw_r = (row & 7) ^ ((row >> 3) & 1);
+                const u32x4 a0 = *reinterpret_cast<const u32x4*>(As + row * BK + ((c0 ^ sw_r) << 4));
+                const u32x4 a1 = *reinterpret_cast<const u32x4*>(As + row * BK + (((c0 + 1) ^ sw_r) << 4));
+                af[i] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const float sw = reinterpret_cast<const float*>(Bs + B_BYTES + NSA * 256)[(wn * CW) / 128];
+            float sr[MI], f[MI];
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                sr[i] = Ss[wm * RW + i * 16 + (lane & 15)];
+                if constexpr (C::LAG < 1) f[i] = sr[i] * sw;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            v4f pp[MI];
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const v8i bf = bnext;
@@ -394,6 +416,7 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
                     for (int i = 0; i < MI; ++i) {
                         const v4f pc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                             bf, af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                        if (j == 1) f[i] = sr[i] * sw;
                         if (j > 0) {
 #pragma unroll
                             for (int v = 0; v < 4; ++v) acc[i][j - 1][v] = fmaf(pp[i][v], f[i], acc[i][j - 1][v]);
