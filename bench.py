@@ -78,6 +78,24 @@ def parse():
     return p.parse_args()
 
 
+def gemm_entry(flop, byts, us, traffic_v):
+    """Roofline entry of one GEMM launch, against whichever peak sets the longer
+    floor for its algorithmic work: the fp8 MFMA peak for its FLOP or the HBM
+    peak for its bytes (arithmetic intensity above or below 625 FLOP/B).  At
+    2048 tokens per source GEMM1 is MFMA-bound (≈830 FLOP/B); at 256 tokens per
+    source its weights dominate and it is HBM-bound (≈120 FLOP/B)."""
+    if flop / (FP8_PEAK_TFLOPS * 1e12) >= byts / (HBM_PEAK_GBS * 1e9):
+        a = flop / (us * 1e-6) / 1e12
+        e = {"bound": "mfma", "achieved": round(a, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(a / FP8_PEAK_TFLOPS, 4)}
+    else:
+        a = byts / (us * 1e-6) / 1e9
+        e = {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(a / HBM_PEAK_GBS, 4)}
+    e.update({"traffic": traffic_v, "algorithmic_flop": int(flop), "algorithmic_bytes": int(byts)})
+    return e
+
+
 def algorithmic(w, R, U, Rc):
     """Bytes (or flops) each kernel must move at minimum, per launch."""
     T, k, H, N, L, E = w.T, w.k, w.H, w.N, w.L, w.E
@@ -202,11 +220,8 @@ def main():
 
     traffic = measured_traffic(args.workload)
     kernels = {n: hbm_entry(n) for n in hbm_names}
-    kernels["gemm1"] = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": FP8_PEAK_TFLOPS,
-                        "unit": "TFLOP/s", "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
-                        "traffic": traffic.get("gemm1"), "us": round(med["gemm1"], 2),
-                        "algorithmic_flop": int(alg["gemm1_flop"]),
-                        "algorithmic_bytes": int(alg["gemm1_bytes"])}
+    kernels["gemm1"] = gemm_entry(alg["gemm1_flop"], alg["gemm1_bytes"], med["gemm1"], traffic.get("gemm1"))
+    kernels["gemm1"]["us"] = round(med["gemm1"], 2)
     dominant = max(names, key=lambda n: med[n])
     roof = {k: v for k, v in kernels[dominant].items() if k in ("bound", "achieved", "peak", "unit", "frac",
                                                                 "traffic")}
@@ -303,7 +318,6 @@ def mx_stage1(torch, moe, w, d, ids_d, x_d, lay, g_ws, alg, traffic, args, fp32_
     stage1 = [sum(per[n][i] for n in names) for i in range(args.steps)]
     stage1_fp32 = [e[0].elapsed_time(e[1]) * 1e3 for e in evf]
     qa = alg["quant_mx"] / (med["quant_mx"] * 1e-6) / 1e9
-    ga = alg["gemm1_flop"] / (med["gemm1_mx"] * 1e-6) / 1e12
     del wq_d, ws_d, q, qs, y
     return {"stage1_us": round(float(np.median(stage1)), 2),
             "stage1_p10_p90_us": [round(float(np.percentile(stage1, 10)), 2),
@@ -315,10 +329,8 @@ def mx_stage1(torch, moe, w, d, ids_d, x_d, lay, g_ws, alg, traffic, args, fp32_
                 "quant_mx": {"bound": "hbm", "achieved": round(qa, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(qa / HBM_PEAK_GBS, 4), "traffic": traffic.get("quant_mx"),
                              "algorithmic_bytes": int(alg["quant_mx"])},
-                "gemm1_mx": {"bound": "mfma", "achieved": round(ga, 1), "peak": FP8_PEAK_TFLOPS,
-                             "unit": "TFLOP/s", "frac": round(ga / FP8_PEAK_TFLOPS, 4),
-                             "traffic": traffic.get("gemm1_mx"), "algorithmic_flop": int(alg["gemm1_flop"]),
-                             "algorithmic_bytes": int(alg["gemm1_mx_bytes"])}}}
+                "gemm1_mx": gemm_entry(alg["gemm1_flop"], alg["gemm1_mx_bytes"], med["gemm1_mx"],
+                                       traffic.get("gemm1_mx"))}}
 
 
 def stage2(torch, moe, w, d, lay, y1, wts_d, alg, traffic, args):
@@ -367,7 +379,6 @@ def stage2(torch, moe, w, d, lay, y1, wts_d, alg, traffic, args):
         return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(a / HBM_PEAK_GBS, 4), "traffic": traffic.get(n), "algorithmic_bytes": int(alg[key])}
 
-    ga = alg["gemm2_flop"] / (med["gemm2"] * 1e-6) / 1e12
 
     # MX variant, A/B against the fp32-scale stage2 on the same GEMM1 output
     t0 = time.time()
@@ -401,7 +412,6 @@ def stage2(torch, moe, w, d, lay, y1, wts_d, alg, traffic, args):
     medm = {n: float(np.median(v)) for n, v in perm.items()}
     totm = [sum(perm[n][i] for n in mx_names) for i in range(args.steps)]
     totf = [e[0].elapsed_time(e[3]) * 1e3 for e in evf]
-    gam = alg["gemm2_flop"] / (medm["gemm2_mx"] * 1e-6) / 1e12
     qam = alg["silu_mul_quant_mx"] / (medm["silu_mul_quant_mx"] * 1e-6) / 1e9
     del w2_d, w2s_d, m2_d, m2s_d, h, hs, hm, hms, y2, out
     mx = {"us_median": round(float(np.median(totm)), 2),
@@ -412,18 +422,14 @@ def stage2(torch, moe, w, d, lay, y1, wts_d, alg, traffic, args):
                                             "unit": "GB/s", "frac": round(qam / HBM_PEAK_GBS, 4),
                                             "traffic": traffic.get("silu_mul_quant_mx"),
                                             "algorithmic_bytes": int(alg["silu_mul_quant_mx"])},
-                      "gemm2_mx": {"bound": "mfma", "achieved": round(gam, 1), "peak": FP8_PEAK_TFLOPS,
-                                   "unit": "TFLOP/s", "frac": round(gam / FP8_PEAK_TFLOPS, 4),
-                                   "traffic": traffic.get("gemm2_mx"), "algorithmic_flop": int(alg["gemm2_flop"]),
-                                   "algorithmic_bytes": int(alg["gemm2_mx_bytes"])}}}
+                      "gemm2_mx": gemm_entry(alg["gemm2_flop"], alg["gemm2_mx_bytes"], medm["gemm2_mx"],
+                                             traffic.get("gemm2_mx"))}}
     return {"us_median": round(float(np.median(tot)), 2),
             "us_p10_p90": [round(float(np.percentile(tot, 10)), 2), round(float(np.percentile(tot, 90)), 2)],
             "inter": I, "kernels_us_median": {n: round(med[n], 2) for n in names},
             "kernels": {"silu_mul_quant": hbm("silu_mul_quant", "silu_mul_quant"),
-                        "gemm2": {"bound": "mfma", "achieved": round(ga, 1), "peak": FP8_PEAK_TFLOPS,
-                                  "unit": "TFLOP/s", "frac": round(ga / FP8_PEAK_TFLOPS, 4),
-                                  "traffic": traffic.get("gemm2"), "algorithmic_flop": int(alg["gemm2_flop"]),
-                                  "algorithmic_bytes": int(alg["gemm2_bytes"])},
+                        "gemm2": gemm_entry(alg["gemm2_flop"], alg["gemm2_bytes"], med["gemm2"],
+                                            traffic.get("gemm2")),
                         "combine_local": hbm("combine_local", "combine_local")},
             "mx": mx}
 

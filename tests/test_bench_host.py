@@ -50,3 +50,16 @@ def test_committed_traffic_summary_parses():
     assert set(got) <= set(ent)
     assert all(isinstance(v, int) and v > 0 for v in got.values())
     assert bench.measured_traffic("tiny_t64_h256_e8") == {}
+
+
+def test_gemm_roofline_bound_follows_arithmetic_intensity():
+    # 2048 tokens per source: ~830 FLOP/B, above the 625 FLOP/B ridge -> MFMA-bound
+    e = bench.gemm_entry(960.5e9, 1.154e9, 500.0, None)
+    assert e["bound"] == "mfma" and e["unit"] == "TFLOP/s"
+    assert abs(e["achieved"] - 960.5e9 / 500e-6 / 1e12) < 0.1
+    assert abs(e["frac"] - e["achieved"] / bench.FP8_PEAK_TFLOPS) < 1e-4
+    # 256 tokens per source: the weights dominate (~120 FLOP/B) -> HBM-bound
+    e = bench.gemm_entry(120e9, 0.967e9, 180.0, 123)
+    assert e["bound"] == "hbm" and e["unit"] == "GB/s" and e["traffic"] == 123
+    assert abs(e["achieved"] - 0.967e9 / 180e-6 / 1e9) < 0.1
+    assert e["algorithmic_flop"] == int(120e9) and e["algorithmic_bytes"] == int(0.967e9)
