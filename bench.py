@@ -208,21 +208,24 @@ def main():
                               for i in range(args.steps)]))
     hbm_names = ("layout_local", "quant", "layout_full", "combine")
     hbm_bytes = sum(alg[n] for n in hbm_names)
-    hbm_time = sum(med[n] for n in hbm_names)
+    # rates (roofline `achieved`, the GB/s and TFLOP/s figures) divide the
+    # algorithmic work by the kernel's average launch duration over the timed steps
+    hbm_time = sum(mean[n] for n in hbm_names)
     hbm_gbs = hbm_bytes / (hbm_time * 1e-6) / 1e9
-    gemm_tflops = alg["gemm1_flop"] / (med["gemm1"] * 1e-6) / 1e12
+    gemm_tflops = alg["gemm1_flop"] / (mean["gemm1"] * 1e-6) / 1e12
 
     def hbm_entry(n):
-        a = alg[n] / (med[n] * 1e-6) / 1e9
+        a = alg[n] / (mean[n] * 1e-6) / 1e9
         return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(a / HBM_PEAK_GBS, 4), "traffic": traffic.get(n), "us": round(med[n], 2),
-                "algorithmic_bytes": int(alg[n])}
+                "frac": round(a / HBM_PEAK_GBS, 4), "traffic": traffic.get(n), "us": round(mean[n], 2),
+                "us_median": round(med[n], 2), "algorithmic_bytes": int(alg[n])}
 
     traffic = measured_traffic(args.workload)
     kernels = {n: hbm_entry(n) for n in hbm_names}
-    kernels["gemm1"] = gemm_entry(alg["gemm1_flop"], alg["gemm1_bytes"], med["gemm1"], traffic.get("gemm1"))
-    kernels["gemm1"]["us"] = round(med["gemm1"], 2)
-    dominant = max(names, key=lambda n: med[n])
+    kernels["gemm1"] = gemm_entry(alg["gemm1_flop"], alg["gemm1_bytes"], mean["gemm1"], traffic.get("gemm1"))
+    kernels["gemm1"]["us"] = round(mean["gemm1"], 2)
+    kernels["gemm1"]["us_median"] = round(med["gemm1"], 2)
+    dominant = max(names, key=lambda n: mean[n])
     roof = {k: v for k, v in kernels[dominant].items() if k in ("bound", "achieved", "peak", "unit", "frac",
                                                                 "traffic")}
     roof["kernel"] = dominant
@@ -315,9 +318,10 @@ def mx_stage1(torch, moe, w, d, ids_d, x_d, lay, g_ws, alg, traffic, args, fp32_
     torch.cuda.synchronize()
     per = {n: [e[j].elapsed_time(e[j + 1]) * 1e3 for e in evs] for j, n in enumerate(names)}
     med = {n: float(np.median(v)) for n, v in per.items()}
+    mean = {n: float(np.mean(v)) for n, v in per.items()}
     stage1 = [sum(per[n][i] for n in names) for i in range(args.steps)]
     stage1_fp32 = [e[0].elapsed_time(e[1]) * 1e3 for e in evf]
-    qa = alg["quant_mx"] / (med["quant_mx"] * 1e-6) / 1e9
+    qa = alg["quant_mx"] / (mean["quant_mx"] * 1e-6) / 1e9
     del wq_d, ws_d, q, qs, y
     return {"stage1_us": round(float(np.median(stage1)), 2),
             "stage1_p10_p90_us": [round(float(np.percentile(stage1, 10)), 2),
@@ -325,11 +329,12 @@ def mx_stage1(torch, moe, w, d, ids_d, x_d, lay, g_ws, alg, traffic, args, fp32_
             "fp32_scale_stage1_us_same_loop": round(float(np.median(stage1_fp32)), 2),
             "mx_over_fp32_stage1": round(float(np.median(stage1)) / float(np.median(stage1_fp32)), 4),
             "kernels_us_median": {n: round(med[n], 2) for n in names},
+            "kernels_us_mean": {n: round(mean[n], 2) for n in names},
             "kernels": {
                 "quant_mx": {"bound": "hbm", "achieved": round(qa, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(qa / HBM_PEAK_GBS, 4), "traffic": traffic.get("quant_mx"),
                              "algorithmic_bytes": int(alg["quant_mx"])},
-                "gemm1_mx": gemm_entry(alg["gemm1_flop"], alg["gemm1_mx_bytes"], med["gemm1_mx"],
+                "gemm1_mx": gemm_entry(alg["gemm1_flop"], alg["gemm1_mx_bytes"], mean["gemm1_mx"],
                                        traffic.get("gemm1_mx"))}}
 
 
@@ -372,10 +377,11 @@ def stage2(torch, moe, w, d, lay, y1, wts_d, alg, traffic, args):
     torch.cuda.synchronize()
     per = {n: [e[j].elapsed_time(e[j + 1]) * 1e3 for e in evs] for j, n in enumerate(names)}
     med = {n: float(np.median(v)) for n, v in per.items()}
+    mean = {n: float(np.mean(v)) for n, v in per.items()}
     tot = [sum(per[n][i] for n in names) for i in range(args.steps)]
 
     def hbm(n, key):
-        a = alg[key] / (med[n] * 1e-6) / 1e9
+        a = alg[key] / (mean[n] * 1e-6) / 1e9
         return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(a / HBM_PEAK_GBS, 4), "traffic": traffic.get(n), "algorithmic_bytes": int(alg[key])}
 
@@ -410,25 +416,28 @@ def stage2(torch, moe, w, d, lay, y1, wts_d, alg, traffic, args):
     torch.cuda.synchronize()
     perm = {n: [e[j].elapsed_time(e[j + 1]) * 1e3 for e in evm] for j, n in enumerate(mx_names)}
     medm = {n: float(np.median(v)) for n, v in perm.items()}
+    meanm = {n: float(np.mean(v)) for n, v in perm.items()}
     totm = [sum(perm[n][i] for n in mx_names) for i in range(args.steps)]
     totf = [e[0].elapsed_time(e[3]) * 1e3 for e in evf]
-    qam = alg["silu_mul_quant_mx"] / (medm["silu_mul_quant_mx"] * 1e-6) / 1e9
+    qam = alg["silu_mul_quant_mx"] / (meanm["silu_mul_quant_mx"] * 1e-6) / 1e9
     del w2_d, w2s_d, m2_d, m2s_d, h, hs, hm, hms, y2, out
     mx = {"us_median": round(float(np.median(totm)), 2),
           "fp32_scale_us_same_loop": round(float(np.median(totf)), 2),
           "mx_over_fp32": round(float(np.median(totm)) / float(np.median(totf)), 4),
           "kernels_us_median": {n: round(medm[n], 2) for n in mx_names},
+          "kernels_us_mean": {n: round(meanm[n], 2) for n in mx_names},
           "kernels": {"silu_mul_quant_mx": {"bound": "hbm", "achieved": round(qam, 1), "peak": HBM_PEAK_GBS,
                                             "unit": "GB/s", "frac": round(qam / HBM_PEAK_GBS, 4),
                                             "traffic": traffic.get("silu_mul_quant_mx"),
                                             "algorithmic_bytes": int(alg["silu_mul_quant_mx"])},
-                      "gemm2_mx": gemm_entry(alg["gemm2_flop"], alg["gemm2_mx_bytes"], medm["gemm2_mx"],
+                      "gemm2_mx": gemm_entry(alg["gemm2_flop"], alg["gemm2_mx_bytes"], meanm["gemm2_mx"],
                                              traffic.get("gemm2_mx"))}}
     return {"us_median": round(float(np.median(tot)), 2),
             "us_p10_p90": [round(float(np.percentile(tot, 10)), 2), round(float(np.percentile(tot, 90)), 2)],
             "inter": I, "kernels_us_median": {n: round(med[n], 2) for n in names},
+            "kernels_us_mean": {n: round(mean[n], 2) for n in names},
             "kernels": {"silu_mul_quant": hbm("silu_mul_quant", "silu_mul_quant"),
-                        "gemm2": gemm_entry(alg["gemm2_flop"], alg["gemm2_bytes"], med["gemm2"],
+                        "gemm2": gemm_entry(alg["gemm2_flop"], alg["gemm2_bytes"], mean["gemm2"],
                                             traffic.get("gemm2")),
                         "combine_local": hbm("combine_local", "combine_local")},
             "mx": mx}
