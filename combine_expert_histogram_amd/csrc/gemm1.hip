@@ -75,6 +75,7 @@ constexpr int kMaxL = 1024;
 constexpr int kXcds = 8;
 constexpr int kMinBM = 128;   // tile descriptors are sized for the smallest row tile
 constexpr int kPrepKb = 8;    // K blocks per row-scale gather work item
+constexpr int kPrepWgPerCu = 4;   // gather workgroups of the pre-pass per CU
 
 #define GPTR(p) ((const void __attribute__((address_space(1)))*)(p))
 #define LPTR(p) ((void __attribute__((address_space(3)))*)(p))
@@ -484,7 +485,9 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
 //    2^-127 on slot 0's payload), as does a weight index outside [0, n_assign).
 //    With e8m0 codes the weights are not folded in (wtab non-null): row r's
 //    weight goes to wtab[r] for the main kernel's epilogue.
-//  * tile descriptors (the last workgroup): per local expert ceil(count / BM)
+//  * tile descriptors (workgroup 0, dispatched first, so its serial work runs
+//    beside the gather instead of after the dispatch of every gather
+//    workgroup): per local expert ceil(count / BM)
 //    row tiles times NT column tiles, experts in order, column tiles outer and
 //    row tiles inner; tiles[0].x = number of tiles, tiles[1 + t] =
 //    {expert, column tile, first row, valid rows | row tile << 9}.
@@ -496,7 +499,7 @@ gemm1_prep_kernel(const uint32_t* __restrict__ q_scale, const int32_t* __restric
                   const int32_t* __restrict__ expert_offsets, int L, int KB, int NT, int64_t T,
                   int64_t rows_cap, int64_t scale_ld, uint32_t* __restrict__ out, int4* __restrict__ tiles,
                   int64_t tiles_cap) {
-    if (blockIdx.x == gridDim.x - 1) {
+    if (blockIdx.x == 0) {
         __shared__ int eoff[kMaxL + 1];
         __shared__ int tstart[kMaxL + 1];
         __shared__ int wsum[256 / MOE_WAVE];
@@ -556,7 +559,7 @@ gemm1_prep_kernel(const uint32_t* __restrict__ q_scale, const int32_t* __restric
     // consecutive rows of one group, so every store instruction is contiguous
     const int KG = (KB + kPrepKb - 1) / kPrepKb;
     const int64_t nthr = (int64_t)(gridDim.x - 1) * 256;
-    for (int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x; item < R * KG; item += nthr) {
+    for (int64_t item = (int64_t)(blockIdx.x - 1) * 256 + threadIdx.x; item < R * KG; item += nthr) {
         const int kg = (int)(item / R);
         const int64_t r = item - (int64_t)kg * R;
         const int s = row_slot ? row_slot[r] : (int)r;
@@ -652,9 +655,12 @@ moe_status run_gemm(const moe::Dims& d, int64_t a_rows, int64_t kdim, int64_t n,
     // MX GEMM2's per-row weights (the fp32 path folds them into the row scales)
     float* wtab = (MX && DIRECT) ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + wl.wtab_off) : nullptr;
     const int NT = (int)((n + BN - 1) / BN);
-    // gather workgroups plus the planning workgroup (the last one)
+    // the planning workgroup (the first one) plus the gather workgroups; the
+    // gather loop strides over the grid, so its size is capped at four
+    // workgroups a CU (the row count R, read on the device, is usually far
+    // below rows_cap)
     const int64_t KG = (KB + kPrepKb - 1) / kPrepKb;
-    const int pgrid = (int)std::min<int64_t>((rows_cap * KG + 255) / 256, 4096) + 1;
+    const int pgrid = (int)std::min<int64_t>((rows_cap * KG + 255) / 256, kPrepWgPerCu * (int64_t)cus) + 1;
     using C = TileCfg;
     hipLaunchKernelGGL((gemm1_prep_kernel<C::BM>), dim3(pgrid), dim3(256), 0, stream, q_scale,
                        DIRECT ? nullptr : row_slot, row_assign, topk_w, rows_cap, wtab, expert_offsets, (int)d.L,

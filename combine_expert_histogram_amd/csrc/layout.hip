@@ -16,7 +16,7 @@
 //           histogram (LDS atomics; order does not matter for counts) and its
 //           landed-token count, written expert-major to the workspace.
 //   place - one workgroup per chunk again.  It reads the whole histogram
-//           (at most ~32K ints, L2-resident) to get, per expert, the rows of
+//           (at most ~32K ints) to get, per expert, the rows of
 //           all earlier chunks and the expert totals, so no separate scan
 //           launch is needed; then each of its four wavefronts ranks the local
 //           assignments of its quarter of the chunk.  A pass takes 64
@@ -34,6 +34,9 @@ constexpr int kBlock = 256;                       // 4 wavefronts
 constexpr int kWaves = kBlock / MOE_WAVE;
 constexpr int64_t kHistTarget = 32768;            // histogram entries aimed for
 constexpr int kMaxLocalExperts = 1024;
+constexpr int kHistBatch = 16;                    // histogram loads a thread keeps in flight
+constexpr int kIdPasses = 4;                      // routing-id passes a wavefront holds in registers
+constexpr int kCountBatch = 8;                    // routing ids a count thread loads before its atomics
 
 struct Plan {
     int64_t CB = 64;   // tokens per chunk (one workgroup)
@@ -98,11 +101,24 @@ layout_count_kernel(const int32_t* __restrict__ ids, int64_t T, int k, int e0, i
 
     const int64_t t0 = (int64_t)c * CB;
     const int64_t t1 = min(T, t0 + CB);
-    for (int64_t a = t0 * k + tid; a < t1 * k; a += kBlock) {
-        const int le = ids[a] - e0;
-        if ((unsigned)le < (unsigned)L) {
-            atomicAdd(&cnt[le], 1);
-            flag[(int)(a / k - t0)] = 1;
+    // a thread's ids are loaded kCountBatch at a time before their atomics, so
+    // the batch costs one memory round trip
+    const int64_t b0 = t0 * k, b1 = t1 * k;
+    for (int64_t base = b0; base < b1; base += (int64_t)kBlock * kCountBatch) {
+        int v[kCountBatch];
+#pragma unroll
+        for (int u = 0; u < kCountBatch; ++u) {
+            const int64_t a = base + u * kBlock + tid;
+            v[u] = a < b1 ? ids[a] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kCountBatch; ++u) {
+            const int64_t a = base + u * kBlock + tid;
+            const int le = v[u] - e0;
+            if (a < b1 && (unsigned)le < (unsigned)L) {
+                atomicAdd(&cnt[le], 1);
+                flag[(int)(a / k - t0)] = 1;
+            }
         }
     }
     __syncthreads();
@@ -150,33 +166,73 @@ layout_place_kernel(const int32_t* __restrict__ ids, int64_t T, int k, int e0, i
     }
     for (int i = tid; i < CB; i += kBlock) flag[i] = 0;
     if (tid < 16) misc[tid] = 0;
+
+    // this chunk's tokens; wave `wave` owns tokens [tw0, tw1), i.e. assignments
+    // [a0, a1), taken 64 at a time (pass p: assignment a0 + 64 p + lane)
+    const int64_t t0 = (int64_t)c * CB;
+    const int64_t t1 = c < NC ? min(T, t0 + CB) : t0;
+    const int CW = CB / kWaves;
+    const int64_t tw0 = min(t1, t0 + (int64_t)wave * CW);
+    const int64_t tw1 = min(t1, tw0 + CW);
+    const int64_t a0 = tw0 * k, a1 = tw1 * k;
+    const int npass = (int)((a1 - a0 + MOE_WAVE - 1) / MOE_WAVE);
+    // the first kIdPasses passes' routing ids, loaded now so that their memory
+    // round trip overlaps the histogram reads (phases 2 and 5 use them; later
+    // passes read ids again there)
+    int idr[kIdPasses];
+#pragma unroll
+    for (int p = 0; p < kIdPasses; ++p) {
+        const int64_t a = a0 + p * MOE_WAVE + lane;
+        idr[p] = a < a1 ? ids[a] : 0;
+    }
     __syncthreads();
 
-    // (1) prefix information from the histogram: each thread takes whole experts
-    // and reads its expert's row (16 B loads, issued together) for the rows of
-    // all earlier chunks (A) and the expert's total (Tt)
+    // (1) prefix information from the histogram: the rows of all earlier chunks
+    // (A) and the expert's total (Tt).  The histogram was written by the count
+    // launch, on every XCD, so these reads miss this XCD's L2; each costs a full
+    // memory round trip.  An expert's row (NCp / 4 int4) is therefore split over
+    // tpe consecutive lanes that issue their loads together (a thread's loads in
+    // batches of kHistBatch), and the lanes' sums are joined by shuffles: with
+    // L = 32 every load of the phase is in flight at once instead of eight
+    // dependent batches per expert.
     {
-        for (int le = tid; le < L; le += kBlock) {
-            const int4* row = reinterpret_cast<const int4*>(hist + (int64_t)le * NCp);
+        const int Q = NCp / 4;
+        int tpe = 1;                                       // lanes per expert: a power of two <= 64
+        while (tpe < MOE_WAVE && tpe * 2 * L <= kBlock && tpe < Q) tpe *= 2;
+        const int sub = tid & (tpe - 1);
+        for (int le0 = 0; le0 < L; le0 += kBlock / tpe) {  // same trip count in every thread
+            const int le = le0 + tid / tpe;
             int sa = 0, st = 0;
-            for (int q0 = 0; q0 < NCp / 4; q0 += 8) {
-                int4 v[8];
+            if (le < L) {
+                const int4* row = reinterpret_cast<const int4*>(hist + (int64_t)le * NCp);
+                for (int q0 = sub; q0 < Q; q0 += kHistBatch * tpe) {
+                    int4 v[kHistBatch];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) v[u] = q0 + u < NCp / 4 ? row[q0 + u] : int4{0, 0, 0, 0};
+                    for (int u = 0; u < kHistBatch; ++u) {
+                        const int qq = q0 + u * tpe;
+                        v[u] = qq < Q ? row[qq] : int4{0, 0, 0, 0};
+                    }
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int cc = (q0 + u) * 4;
-                    const int e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+                    for (int u = 0; u < kHistBatch; ++u) {
+                        const int cc = (q0 + u * tpe) * 4;
+                        const int e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
-                    for (int z = 0; z < 4; ++z) {
-                        const int val = cc + z < NC ? e[z] : 0;     // stride padding is not written
-                        st += val;
-                        if (cc + z < c) sa += val;
+                        for (int z = 0; z < 4; ++z) {
+                            const int val = cc + z < NC ? e[z] : 0;     // stride padding is not written
+                            st += val;
+                            if (cc + z < c) sa += val;
+                        }
                     }
                 }
             }
-            A[le] = sa;
-            Tt[le] = st;
+            for (int off = tpe / 2; off > 0; off >>= 1) {
+                sa += __shfl_xor(sa, off, MOE_WAVE);
+                st += __shfl_xor(st, off, MOE_WAVE);
+            }
+            if (le < L && sub == 0) {
+                A[le] = sa;
+                Tt[le] = st;
+            }
         }
         int lb = 0, lt = 0;
         for (int j = tid; j < NC; j += kBlock) {
@@ -192,18 +248,20 @@ layout_place_kernel(const int32_t* __restrict__ ids, int64_t T, int k, int e0, i
         }
     }
 
-    // (2) this chunk: wave `wave` owns tokens [tw0, tw1)
-    const int64_t t0 = (int64_t)c * CB;
-    const int64_t t1 = c < NC ? min(T, t0 + CB) : t0;
-    const int CW = CB / kWaves;
-    const int64_t tw0 = min(t1, t0 + (int64_t)wave * CW);
-    const int64_t tw1 = min(t1, tw0 + CW);
-    for (int64_t a = tw0 * k + lane; a < tw1 * k; a += MOE_WAVE) {
-        const int le = ids[a] - e0;
-        if ((unsigned)le < (unsigned)L) {
+    // (2) this wave's per-expert counts and the chunk's landed flags
+    auto count_one = [&](int64_t a, int id) __attribute__((always_inline)) {
+        const int le = id - e0;
+        if (a < a1 && (unsigned)le < (unsigned)L) {
             atomicAdd(&wcnt[le], 1);
             flag[(int)(a / k - t0)] = 1;
         }
+    };
+#pragma unroll
+    for (int p = 0; p < kIdPasses; ++p)
+        if (p < npass) count_one(a0 + p * MOE_WAVE + lane, idr[p]);
+    for (int p = kIdPasses; p < npass; ++p) {
+        const int64_t a = a0 + p * MOE_WAVE + lane;
+        count_one(a, a < a1 ? ids[a] : 0);
     }
     __syncthreads();
 
@@ -277,10 +335,9 @@ layout_place_kernel(const int32_t* __restrict__ ids, int64_t T, int k, int e0, i
     wave_sync_lds();
 
     // (5) rows: stable rank of each local assignment within its expert
-    for (int64_t ab = tw0 * k; ab < tw1 * k; ab += MOE_WAVE) {
-        const int64_t a = ab + lane;
-        const bool valid = a < tw1 * k;
-        const int le = valid ? ids[a] - e0 : -1;
+    auto place_one = [&](int64_t a, int id) __attribute__((always_inline)) {
+        const bool valid = a < a1;
+        const int le = valid ? id - e0 : -1;
         const bool loc = valid && (unsigned)le < (unsigned)L;
         if (loc) atomicOr(reinterpret_cast<unsigned long long*>(&mask[le]), 1ull << lane);
         wave_sync_lds();
@@ -306,6 +363,13 @@ layout_place_kernel(const int32_t* __restrict__ ids, int64_t T, int k, int e0, i
             assign_row[a] = -1;
         }
         wave_sync_lds();
+    };
+#pragma unroll
+    for (int p = 0; p < kIdPasses; ++p)
+        if (p < npass) place_one(a0 + p * MOE_WAVE + lane, idr[p]);
+    for (int p = kIdPasses; p < npass; ++p) {
+        const int64_t a = a0 + p * MOE_WAVE + lane;
+        place_one(a, a < a1 ? ids[a] : 0);
     }
 }
 
