@@ -3,23 +3,31 @@
 // silu(gate) * up rows): a block is held by 8 adjacent lanes, 16 values each.
 //
 // Bit-exactness: the definition is e4m3(x / s), s = amax / 448, with IEEE
-// divisions.  encode_block16 computes w = x * (1/s) (both roundings to
-// nearest) and encodes w with the hardware conversion (v_cvt_pk_fp8_f32: OCP
-// e4m3, round to nearest even; every |w| here is below the 464 rounding
-// boundary, so no saturation case arises), unless w lies within 8 fp32 ulps
-// of an e4m3 rounding tie, or in the e4m3 subnormal range (|w| < 2^-6,
-// nonzero): such elements (rare; the lane takes one divergent branch) redo the
-// IEEE division x / s.  Bound: 1/s and the product each carry <= 2^-24
-// relative error, so |w - x/s| <= 2 ulp(x/s), and the correctly rounded
-// quotient is within 0.5 ulp of x/s, so outside the window both round to the
-// same code.
+// divisions.  Neither division is done on the fast path:
+//  * s: s0 = amax * c with c = fl(1/448); the residual amax - 448 * s0 is exact
+//    in fp32 (one fma), and s = fma(residual, c, s0) is the correctly rounded
+//    quotient.  Checked exhaustively against the IEEE quotient for every fp32
+//    mantissa of a binade (and exactly, in rational arithmetic, for every
+//    bf16 amax); the result scales by powers of two, so it holds for every
+//    amax >= 2^-100, where no intermediate is subnormal.  Smaller maxima take
+//    the IEEE division.
+//  * x / s is bracketed instead: r = 1/s to within a few 2^-24 (v_rcp_f32 and
+//    one Newton step), r_hi = r * (1 + 2^-20) and r_lo = r * (1 - 2^-20)
+//    satisfy r_lo <= 1/s <= r_hi, so x * r_lo <= x / s <= x * r_hi for x >= 0
+//    (reversed for x < 0), and rounding to fp32 keeps that order.  The
+//    hardware conversion (v_cvt_pk_fp8_f32: OCP e4m3, round to nearest even,
+//    subnormal results included) is monotone, so when the codes of x * r_lo
+//    and x * r_hi agree, the code of the IEEE quotient is the same one.  They
+//    differ only when a rounding boundary of e4m3 lies in the 2^-19-wide
+//    bracket (about one element in 5 * 10^4); a lane holding such an element
+//    redoes its 16 values with the IEEE division.  Every |x * r_hi| is below
+//    448 * (1 + 2^-19), far under the 464 rounding boundary, so no saturation
+//    case arises.
 #pragma once
 
 #include "common.h"
 
 namespace moe {
-
-constexpr uint32_t kE4m3MinNormalBits = 0x3C800000u;   // 2^-6, smallest e4m3 normal
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t v) {
@@ -35,15 +43,6 @@ __device__ __forceinline__ uint32_t group8_max(uint32_t v) {
     return v;
 }
 
-// True when w might round differently from the IEEE quotient: within 8 ulps
-// of an e4m3 rounding tie in the normal range, or a nonzero e4m3 subnormal.
-__device__ __forceinline__ bool needs_exact(float w) {
-    const uint32_t ab = __float_as_uint(w) & 0x7FFFFFFFu;
-    const bool tie = ((ab & 0xFFFFFu) - 0x7FFF8u) < 16u;
-    const bool sub = (ab - 1u) < (kE4m3MinNormalBits - 1u);
-    return tie | sub;
-}
-
 // four e4m3 codes of (a, b, c, d), hardware round to nearest even
 __device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
     int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
@@ -51,31 +50,46 @@ __device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
     return (uint32_t)v;
 }
 
+// s = amax / 448 rounded to nearest even, for amax >= 2^-100 (see above)
+__device__ __forceinline__ float div448(float amax) {
+    constexpr float c = 0x1.24924ap-9f;                  // fl(1/448)
+    const float s0 = __fmul_rn(amax, c);
+    const float rem = fmaf(-s0, 448.0f, amax);           // exact
+    return fmaf(rem, c, s0);
+}
+
 // Codes of this lane's 16 values of a block whose |max| over all its 128
 // values is amax (the same in the block's 8 lanes): out[i] holds the codes of
 // x[4i .. 4i+3], byte j = x[4i+j].  Returns the block's scale s = amax / 448
 // (0 for an all-zero block, whose codes are 0).
 __device__ __forceinline__ float encode_block16(const float (&xv)[16], float amax, uint32_t (&out)[4]) {
-    const float s = amax / 448.0f;
-    const float r = 1.0f / s;
     const bool zero = amax == 0.0f;
-    // a scale too small for 1/s to be finite takes the exact division throughout
-    const bool all_exact = !(r <= 3.0e38f);
-    float w[16];
-    bool slow = all_exact;
+    // maxima below 2^-100 (rare: the workloads never produce them) take the IEEE
+    // divisions throughout
+    const bool tiny = !(amax >= 0x1p-100f);
+    float s;
+    if (__builtin_expect(tiny, 0)) s = amax / 448.0f;
+    else s = div448(amax);
+    const float r0 = __builtin_amdgcn_rcpf(s);
+    const float r = fmaf(r0, fmaf(-s, r0, 1.0f), r0);
+    const float r_hi = __fmul_rn(r, 1.0f + 0x1p-20f), r_lo = __fmul_rn(r, 1.0f - 0x1p-20f);
+    bool slow = tiny;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        w[i] = __fmul_rn(xv[i], r);
-        slow |= needs_exact(w[i]);
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t hi = cvt4(__fmul_rn(xv[4 * i], r_hi), __fmul_rn(xv[4 * i + 1], r_hi),
+                                 __fmul_rn(xv[4 * i + 2], r_hi), __fmul_rn(xv[4 * i + 3], r_hi));
+        const uint32_t lo = cvt4(__fmul_rn(xv[4 * i], r_lo), __fmul_rn(xv[4 * i + 1], r_lo),
+                                 __fmul_rn(xv[4 * i + 2], r_lo), __fmul_rn(xv[4 * i + 3], r_lo));
+        slow |= hi != lo;
+        out[i] = hi;
     }
-    if (slow) {
+    if (slow && !zero) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            if (all_exact || needs_exact(w[i])) w[i] = xv[i] / s;
+        for (int i = 0; i < 4; ++i)
+            out[i] = cvt4(xv[4 * i] / s, xv[4 * i + 1] / s, xv[4 * i + 2] / s, xv[4 * i + 3] / s);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        out[i] = zero ? 0u : cvt4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+    for (int i = 0; i < 4; ++i) out[i] = zero ? 0u : out[i];
     return zero ? 0.0f : s;
 }
 
