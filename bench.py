@@ -49,7 +49,6 @@ TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_step_ep8_2048x8_h7
 def measured_traffic(workload: str) -> dict:
     """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE counter summary, per
     bench entry, for entries whose kernel source still hashes to what was profiled."""
-    import hashlib
     import re
     if workload != "ep8_2048x8_h7168" or not os.path.exists(TRAFFIC_PROFILE):
         return {}
@@ -58,12 +57,21 @@ def measured_traffic(workload: str) -> dict:
         return {}
     out = {}
     for name, e in json.loads(m.group(1))["entries"].items():
-        h = hashlib.sha256()
-        for f in ("common.h", os.path.basename(e["source"])):
-            h.update(open(os.path.join(ROOT, "combine_expert_histogram_amd", "csrc", f), "rb").read())
-        if h.hexdigest() == e["source_sha256"]:
+        if source_sha256(e["source"]) == e["source_sha256"]:
             out[name] = int(e["bytes"])
     return out
+
+
+def source_sha256(source: str) -> str:
+    """SHA-256 over every header of the kernel sources (sorted by name), then the
+    kernel's own file: a change to any code the kernel is built from changes it."""
+    import glob
+    import hashlib
+    csrc = os.path.join(ROOT, "combine_expert_histogram_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(csrc, "*.h"))) + [os.path.join(csrc, os.path.basename(source))]:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def parse():
