@@ -278,6 +278,10 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
     }
 
     // ---------------- compute wavefronts ----------------
+    // issue priority over the loaders, which mostly sleep on their waits: when
+    // both are ready the SIMD serves the MFMA stream first (≈1 % faster in
+    // interleaved timing of GEMM1 and GEMM2; loader priority measured ±0)
+    __builtin_amdgcn_s_setprio(2);
     const int wm = wave / WN, wn = wave % WN;
     int g = 0;
     for (int it = 0; it < ntiles; ++it) {
