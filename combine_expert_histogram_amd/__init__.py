@@ -10,7 +10,7 @@ the ctypes layer that passes torch device tensors and torch's current stream.
 from .binding import (  # noqa: F401
     Dims, MoeError, alloc_gemm1_workspace, alloc_layout, combine, grouped_gemm1, lib, moe_capacity, moe_combine,
     grouped_gemm1_mx, moe_grouped_gemm1, moe_grouped_gemm1_mx, moe_grouped_gemm1_workspace, moe_quant_dispatch,
-    moe_quant_dispatch_mx, moe_route_layout, moe_route_layout_workspace, moe_status_string, quant_dispatch,
+    moe_quant_dispatch_mx, moe_route_layout, moe_route_layout_noalloc, moe_route_layout_workspace, moe_status_string, quant_dispatch,
     quant_dispatch_mx, route_layout, silu_mul_quant, grouped_gemm2, alloc_gemm2_workspace, moe_silu_mul_quant,
     moe_grouped_gemm2, moe_grouped_gemm2_workspace, silu_mul_quant_mx, grouped_gemm2_mx, moe_silu_mul_quant_mx,
     moe_grouped_gemm2_mx,

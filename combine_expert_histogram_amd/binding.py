@@ -22,6 +22,7 @@ _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_WORKSPACE",
 
 # every symbol include/moe_hotpath.h declares
 EXPORTS = ("moe_status_string", "moe_capacity", "moe_route_layout_workspace", "moe_route_layout",
+           "moe_route_layout_noalloc",
            "moe_quant_dispatch", "moe_grouped_gemm1_workspace", "moe_grouped_gemm1",
            "moe_quant_dispatch_mx", "moe_grouped_gemm1_mx", "moe_silu_mul_quant",
            "moe_grouped_gemm2_workspace", "moe_grouped_gemm2", "moe_silu_mul_quant_mx",
@@ -77,6 +78,7 @@ def lib() -> ctypes.CDLL:
             "moe_capacity": (I32, [D, ctypes.POINTER(I64), ctypes.POINTER(I64)]),
             "moe_route_layout_workspace": (I32, [D, ctypes.POINTER(SZ)]),
             "moe_route_layout": (I32, [D] + [P] * 10 + [P, SZ, P]),
+            "moe_route_layout_noalloc": (I32, [D] + [P] * 10 + [P]),
             "moe_quant_dispatch": (I32, [D, P, P, P, P, P, P]),
             "moe_grouped_gemm1_workspace": (I32, [D, I32, ctypes.POINTER(SZ)]),
             "moe_grouped_gemm1": (I32, [D, I32] + [P] * 8 + [P, SZ, P]),
@@ -162,6 +164,19 @@ def moe_route_layout(d: Dims, topk_ids, expert_counts, expert_offsets, row_slot,
         _i32(src_slot_offsets, "src_slot_offsets", S + 1), _i32(totals, "totals", 2),
         _ptr(ws, "ws", ws_need), 0 if ws is None else ws.numel() * ws.element_size(), _stream())
     _check("moe_route_layout", st)
+
+
+def moe_route_layout_noalloc(d: Dims, topk_ids, expert_counts, expert_offsets, row_slot, row_assign,
+                             assign_row, tok_slot, slot_tok, src_slot_offsets, totals) -> None:
+    T, k, L, S = d.T, d.k, d.L, d.S
+    rows_cap, slots_cap = T * k, T
+    st = lib().moe_route_layout_noalloc(
+        ctypes.byref(d.c()), _i32(topk_ids, "topk_ids", T * k), _i32(expert_counts, "expert_counts", L),
+        _i32(expert_offsets, "expert_offsets", L + 1), _i32(row_slot, "row_slot", rows_cap),
+        _i32(row_assign, "row_assign", rows_cap), _i32(assign_row, "assign_row", T * k),
+        _i32(tok_slot, "tok_slot", T), _i32(slot_tok, "slot_tok", slots_cap),
+        _i32(src_slot_offsets, "src_slot_offsets", S + 1), _i32(totals, "totals", 2), _stream())
+    _check("moe_route_layout_noalloc", st)
 
 
 def moe_quant_dispatch(d: Dims, x_bf16, slot_tok, totals, q_e4m3, q_scale) -> None:

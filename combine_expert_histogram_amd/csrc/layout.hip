@@ -26,6 +26,8 @@
 //           whatever the number of distinct experts in it.
 #include "common.h"
 
+#include <mutex>
+
 namespace {
 
 using moe::Dims;
@@ -373,6 +375,76 @@ layout_place_kernel(const int32_t* __restrict__ ids, int64_t T, int k, int e0, i
     }
 }
 
+// Validates the layout call's arguments and sizes its plan; no HIP call.
+moe_status check_layout(const moe_dims* dims, const int32_t* topk_ids, int32_t* expert_counts,
+                        int32_t* expert_offsets, int32_t* row_slot, int32_t* row_assign, int32_t* assign_row,
+                        int32_t* tok_slot, int32_t* slot_tok, int32_t* src_slot_offsets, int32_t* totals,
+                        Dims* d, Plan* p) {
+    moe_status st = moe::load_dims(dims, d, false);
+    if (st != MOE_OK) return st;
+    if (d->L > kMaxLocalExperts) return MOE_ERR_UNSUPPORTED;
+    if (!expert_counts || !expert_offsets || !src_slot_offsets || !totals) return MOE_ERR_INVALID_ARG;
+    if (d->T > 0 && (!topk_ids || !row_slot || !row_assign || !assign_row || !tok_slot || !slot_tok))
+        return MOE_ERR_INVALID_ARG;
+    *p = make_plan(*d);
+    if (p->NCp * d->L >= INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+// The two launches on `stream`, with the histogram and landed counts in ws.
+moe_status launch_layout(const Dims& d, const Plan& p, const int32_t* topk_ids, int32_t* expert_counts,
+                         int32_t* expert_offsets, int32_t* row_slot, int32_t* row_assign, int32_t* assign_row,
+                         int32_t* tok_slot, int32_t* slot_tok, int32_t* src_slot_offsets, int32_t* totals,
+                         int32_t* ws, hipStream_t stream) {
+    moe_status st;
+    int32_t* hist = ws + p.off_hist;
+    int32_t* landed = ws + p.off_landed;
+    if (p.NC > 0) {
+        hipLaunchKernelGGL(layout_count_kernel, dim3((unsigned)p.NC), dim3(kBlock), count_lds(d, p),
+                           stream, topk_ids, d.T, (int)d.k, (int)d.e0, (int)d.L, (int)p.CB, (int)p.NCp,
+                           hist, landed);
+        if ((st = moe::launch_status()) != MOE_OK) return st;
+    }
+    // at least one workgroup, so that T == 0 still writes the counts and totals
+    const unsigned grid = (unsigned)std::max<int64_t>(p.NC, 1);
+    hipLaunchKernelGGL(layout_place_kernel, dim3(grid), dim3(kBlock), place_lds(d.L, p.CB).total,
+                       stream, topk_ids, d.T, (int)d.k, (int)d.e0, (int)d.L, (int)p.CB, (int)p.NC,
+                       (int)p.NCp, (int)d.S, d.Ts, hist, landed, expert_counts, expert_offsets, row_slot,
+                       row_assign, assign_row, tok_slot, slot_tok, src_slot_offsets, totals);
+    return moe::launch_status();
+}
+
+// ------------------------------------------------ allocation-free variant
+// The layout's workspace (the per-chunk histogram and landed counts) in a
+// static device array instead of a caller-provided buffer, for callers that
+// cannot allocate.  Every GPU the library runs on holds its own copy of the
+// array until the process ends.  It needs no clearing between calls: the count
+// launch writes every histogram entry and landed count that the place launch
+// reads (the histogram's row padding is never read).
+constexpr int64_t kScratchInts = 65536;                   // 256 KiB
+static __device__ __align__(256) int32_t scratch[kScratchInts];
+
+// Device address of `scratch` on each device, looked up once per device with
+// that device current.  In host code `scratch` names a host-side stand-in, so
+// kernels only ever receive these addresses.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kMaxDevices] = {};
+
+moe_status scratch_address(int32_t** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+        g_scratch_addr[dev] = p;
+    }
+    *out = static_cast<int32_t*>(g_scratch_addr[dev]);
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" moe_status moe_capacity(const moe_dims* dims, int64_t* rows_cap, int64_t* slots_cap) {
@@ -402,31 +474,29 @@ extern "C" moe_status moe_route_layout(const moe_dims* dims, const int32_t* topk
                                        int32_t* src_slot_offsets, int32_t* totals, void* ws,
                                        size_t ws_bytes, void* hip_stream) {
     Dims d;
-    moe_status st = moe::load_dims(dims, &d, false);
+    Plan p;
+    moe_status st = check_layout(dims, topk_ids, expert_counts, expert_offsets, row_slot, row_assign, assign_row,
+                                 tok_slot, slot_tok, src_slot_offsets, totals, &d, &p);
     if (st != MOE_OK) return st;
-    if (d.L > kMaxLocalExperts) return MOE_ERR_UNSUPPORTED;
-    if (!expert_counts || !expert_offsets || !src_slot_offsets || !totals) return MOE_ERR_INVALID_ARG;
-    if (d.T > 0 && (!topk_ids || !row_slot || !row_assign || !assign_row || !tok_slot || !slot_tok))
-        return MOE_ERR_INVALID_ARG;
-    const Plan p = make_plan(d);
     if (!ws || ws_bytes < (size_t)p.total_ints * 4) return MOE_ERR_WORKSPACE;
-    if (p.NCp * d.L >= INT32_MAX) return MOE_ERR_UNSUPPORTED;
-    hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
-    int32_t* w = reinterpret_cast<int32_t*>(ws);
-    int32_t* hist = w + p.off_hist;
-    int32_t* landed = w + p.off_landed;
+    return launch_layout(d, p, topk_ids, expert_counts, expert_offsets, row_slot, row_assign, assign_row, tok_slot,
+                         slot_tok, src_slot_offsets, totals, reinterpret_cast<int32_t*>(ws),
+                         reinterpret_cast<hipStream_t>(hip_stream));
+}
 
-    if (p.NC > 0) {
-        hipLaunchKernelGGL(layout_count_kernel, dim3((unsigned)p.NC), dim3(kBlock), count_lds(d, p),
-                           stream, topk_ids, d.T, (int)d.k, (int)d.e0, (int)d.L, (int)p.CB, (int)p.NCp,
-                           hist, landed);
-        if ((st = moe::launch_status()) != MOE_OK) return st;
-    }
-    // at least one workgroup, so that T == 0 still writes the counts and totals
-    const unsigned grid = (unsigned)std::max<int64_t>(p.NC, 1);
-    hipLaunchKernelGGL(layout_place_kernel, dim3(grid), dim3(kBlock), place_lds(d.L, p.CB).total,
-                       stream, topk_ids, d.T, (int)d.k, (int)d.e0, (int)d.L, (int)p.CB, (int)p.NC,
-                       (int)p.NCp, (int)d.S, d.Ts, hist, landed, expert_counts, expert_offsets, row_slot,
-                       row_assign, assign_row, tok_slot, slot_tok, src_slot_offsets, totals);
-    return moe::launch_status();
+extern "C" moe_status moe_route_layout_noalloc(const moe_dims* dims, const int32_t* topk_ids,
+                                               int32_t* expert_counts, int32_t* expert_offsets,
+                                               int32_t* row_slot, int32_t* row_assign, int32_t* assign_row,
+                                               int32_t* tok_slot, int32_t* slot_tok,
+                                               int32_t* src_slot_offsets, int32_t* totals, void* hip_stream) {
+    Dims d;
+    Plan p;
+    moe_status st = check_layout(dims, topk_ids, expert_counts, expert_offsets, row_slot, row_assign, assign_row,
+                                 tok_slot, slot_tok, src_slot_offsets, totals, &d, &p);
+    if (st != MOE_OK) return st;
+    if (p.total_ints > kScratchInts) return MOE_ERR_WORKSPACE;   // the static array is too small
+    int32_t* ws = nullptr;
+    if ((st = scratch_address(&ws)) != MOE_OK) return st;
+    return launch_layout(d, p, topk_ids, expert_counts, expert_offsets, row_slot, row_assign, assign_row, tok_slot,
+                         slot_tok, src_slot_offsets, totals, ws, reinterpret_cast<hipStream_t>(hip_stream));
 }

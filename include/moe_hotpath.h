@@ -113,6 +113,30 @@ moe_status moe_route_layout(const moe_dims* dims, const int32_t* topk_ids,
                             int32_t* totals, void* ws, size_t ws_bytes, void* hip_stream);
 
 /*
+ * Allocation-free variant of moe_route_layout, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, outputs and results as
+ * moe_route_layout, without the workspace: the layout's histogram and landed
+ * counts live in a static device array of the library, 256 KiB per GPU,
+ * held on each GPU the library runs on until the process ends.
+ *   - The call allocates nothing; its first call on a device looks up that
+ *     device's copy of the array (no allocation).
+ *   - Returns MOE_ERR_WORKSPACE when the layout needs more than the array holds
+ *     (moe_route_layout_workspace(dims) > 262144 bytes; every configuration
+ *     with T*L <= 2^22 fits, e.g. 16384 tokens over 256 local experts uses
+ *     132 KiB).  Nothing is launched then.
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap in
+ *     time on one GPU (on different streams, or from different host threads)
+ *     race and give undefined results; serialise them, e.g. on one stream.
+ *     The array needs no clearing: each call writes every entry it reads.
+ */
+moe_status moe_route_layout_noalloc(const moe_dims* dims, const int32_t* topk_ids,
+                                    int32_t* expert_counts, int32_t* expert_offsets,
+                                    int32_t* row_slot, int32_t* row_assign, int32_t* assign_row,
+                                    int32_t* tok_slot, int32_t* slot_tok, int32_t* src_slot_offsets,
+                                    int32_t* totals, void* hip_stream);
+
+/*
  * Step 2: quant + dispatch.  Each landed token's row is read once and
  * quantised once into its slot ("MegaMoE stage1 dispatch over SDMA", commit
  * "each token read and quantised once"; "How it works now": the quant writes

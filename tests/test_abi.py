@@ -152,3 +152,24 @@ def test_stage2_and_mx_empty_input_calls_are_noops(L):
     assert L.moe_grouped_gemm2(ctypes.byref(d), 128, *([None] * 8), None, 0, None) == 0
     assert L.moe_silu_mul_quant_mx(ctypes.byref(d), 128, None, None, None, None, None) == 0
     assert L.moe_grouped_gemm2_mx(ctypes.byref(d), 128, *([None] * 8), None, 0, None) == 0
+
+
+def test_noalloc_layout_size_limit(L):
+    """The allocation-free layout holds its workspace in a 256 KiB static array:
+    every configuration with T*L <= 2^22 fits it, and a larger one is refused
+    with MOE_ERR_WORKSPACE before anything touches the GPU."""
+    from combine_expert_histogram_amd import binding as b
+    cap = 256 * 1024
+    for S, Ts, Lx in ((1, 1 << 21, 1), (1, (1 << 21) - 64, 1), (2, 1 << 20, 2), (8, 2048, 256),
+                      (8, 8192, 32), (4, 1024, 1024), (1, 4096, 1000), (8, 2048, 32)):
+        d = b.Dims(S=S, Ts=Ts, k=min(8, Lx), E=max(Lx, 8), e0=0, L=Lx)
+        assert S * Ts * Lx <= 1 << 22
+        assert b.moe_route_layout_workspace(d) <= cap, (S, Ts, Lx)
+    big = b.Dims(S=8, Ts=1 << 17, k=8, E=1024, e0=0, L=1024)
+    assert b.moe_route_layout_workspace(big) > cap
+    P = ctypes.c_void_p
+    fake = P(4096)   # never dereferenced: the size check comes first
+    assert L.moe_route_layout_noalloc(ctypes.byref(big.c()), *([fake] * 10), None) == -2
+    # null outputs are refused like moe_route_layout's
+    small = b.Dims(S=1, Ts=64, k=2, E=8, e0=0, L=8)
+    assert L.moe_route_layout_noalloc(ctypes.byref(small.c()), fake, *([None] * 9), None) == -1
