@@ -1,7 +1,11 @@
-// Measurement aid, not part of the hot path's C ABI (built as a separate
-// library, libmoe_ceiling.so, loaded only by the benchmark): a kernel that does
-// nothing but fp8 MFMAs, so the benchmark can report the MFMA rate this chip
-// sustains in the same run next to the grouped GEMM1's rate.
+// Measurement aids, not part of the hot path's C ABI (built as a separate
+// library, libmoe_ceiling.so, loaded only by the benchmark):
+//  * a kernel that does nothing but fp8 MFMAs, so the benchmark can report the
+//    MFMA rate this chip sustains in the same run next to the grouped GEMM1's;
+//  * a read stream: one pass of non-temporal 16 B loads over a buffer (4 loads
+//    in flight per lane), folded into one word per thread, so the benchmark can
+//    report the HBM read rate this chip sustains (the hot path's HBM-bound
+//    kernels mostly read: the combine reads 9 bytes for each one it writes).
 //
 // Each wavefront keeps 16 independent 16x16x128 fp8 MFMA accumulators and
 // runs `iters` rounds of 16 MFMAs (the operands vary with the lane and the
@@ -36,7 +40,39 @@ __global__ void __launch_bounds__(512) mfma_loop_kernel(int iters, float* out) {
     out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ void __launch_bounds__(256) read_stream_kernel(const u32x4* __restrict__ p, int64_t n16,
+                                                          uint32_t* __restrict__ out) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const u32x4 a = __builtin_nontemporal_load(p + i);
+        const u32x4 b = __builtin_nontemporal_load(p + i + stride);
+        const u32x4 c = __builtin_nontemporal_load(p + i + 2 * stride);
+        const u32x4 d = __builtin_nontemporal_load(p + i + 3 * stride);
+        acc ^= (a.x ^ a.y ^ a.z ^ a.w) ^ (b.x ^ b.y ^ b.z ^ b.w) ^ (c.x ^ c.y ^ c.z ^ c.w) ^ (d.x ^ d.y ^ d.z ^ d.w);
+    }
+    for (; i < n16; i += stride) {
+        const u32x4 a = __builtin_nontemporal_load(p + i);
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
 }  // namespace
+
+// Reads `bytes` (a multiple of 16) from the device buffer `buf` once with grid
+// workgroups of 256 threads on `hip_stream`; `out` holds grid * 256 words.
+// Returns 0, or -1 for bad arguments / a launch error.
+extern "C" int moe_ceiling_read_stream(const void* buf, int64_t bytes, int grid, uint32_t* out,
+                                       void* hip_stream) {
+    if (!buf || !out || grid <= 0 || bytes <= 0 || bytes % 16 != 0) return -1;
+    hipLaunchKernelGGL(read_stream_kernel, dim3(grid), dim3(256), 0, reinterpret_cast<hipStream_t>(hip_stream),
+                       static_cast<const u32x4*>(buf), bytes / 16, out);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
 
 // Launches grid workgroups of 512 threads on `hip_stream`; `out` holds
 // grid * 512 floats.  FLOP per launch = grid * 8 * iters * 16 * 65536.

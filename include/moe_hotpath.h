@@ -172,8 +172,10 @@ moe_status moe_grouped_gemm1_workspace(const moe_dims* dims, int32_t n, size_t* 
  *   y[r, c] = bf16( sum_h  q[row_slot[r], h] * q_scale[row_slot[r], h/128]
  *                        * w[le, c, h]    * w_scale[le, c/128, h/128] )
  * accumulated in fp32 (fp8 MFMA per 128-wide K block, then scaled).
- * In:  q_e4m3, q_scale from step 2; row_slot, expert_offsets, totals from
- *      step 1 (expert_offsets and totals are read on the device);
+ * In:  q_e4m3, q_scale from step 2; row_slot, expert_offsets from step 1
+ *      (expert_offsets is read on the device: R = expert_offsets[L]);
+ *      totals: accepted for symmetry with the other calls and not read (may
+ *      be NULL);
  *      w_e4m3  uint8 [L, n, H]  (each expert's weight stored K-contiguous:
  *              element (h, c) of the logical [H, n] weight at [le, c, h]);
  *      w_scale float32 [L, n/128, H/128]  one scale per 128x128 block.

@@ -4,6 +4,7 @@ from __future__ import annotations
 
 import functools
 import sys
+from typing import NamedTuple
 
 import numpy as np
 import torch
@@ -95,14 +96,30 @@ def bf16_half_ulp(r: np.ndarray) -> np.ndarray:
     return np.exp2(e - 8)
 
 
-def tolerance(got_bits: np.ndarray, ref_f32: np.ndarray):
-    """(ok, rel_l2, max_excess, rms) of a bf16 result against an fp32 reference.
+class Tol(NamedTuple):
+    """A bf16 result against an fp32 reference: the verdict and the figures."""
+    ok: bool
+    rel_l2: float
+    max_excess: float     # max(|err| - half a bf16 ulp of the reference): the bound's subject
+    rms: float            # rms of the reference
+    max_abs: float        # the literal max |err|
+
+    def __str__(self):
+        r = self.rms if self.rms > 0 else 1.0
+        return (f"rel_l2={self.rel_l2:.3e} max_abs={self.max_abs:.3e} ({self.max_abs / r:.4f} rms) "
+                f"max_abs_beyond_half_ulp={self.max_excess:.3e} ({self.max_excess / r:.4f} rms) "
+                f"rms={self.rms:.3e} ok={self.ok}")
+
+
+def tolerance(got_bits: np.ndarray, ref_f32: np.ndarray) -> Tol:
+    """A bf16 result against an fp32 reference.
 
     rel-L2 <= 1e-2, and every element within 2e-2 * rms(reference) beyond the
     half-ulp rounding of the bf16 output format itself: bf16 keeps 8
     significant bits, so rounding the exact value alone costs up to
     2^-8 * |y|, which exceeds 2e-2 * rms once |y| > 5.12 * rms; the max-abs
-    bound is applied to the error on top of that rounding."""
+    bound is applied to the error on top of that rounding.  The literal
+    max |err| is returned (and printed by the tests) beside it."""
     g = obf16.to_f32(got_bits).astype(np.float64)
     r = np.asarray(ref_f32, dtype=np.float64)
     diff = g - r
@@ -111,5 +128,6 @@ def tolerance(got_bits: np.ndarray, ref_f32: np.ndarray):
     rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
     excess = np.abs(diff) - bf16_half_ulp(r)
     mx = float(excess.max()) if r.size else 0.0
+    mabs = float(np.abs(diff).max()) if r.size else 0.0
     ok = rel <= REL_L2_TOL and mx <= MAX_ABS_TOL * rms + 1e-30
-    return ok, float(rel), mx, rms
+    return Tol(bool(ok), float(rel), mx, rms, mabs)

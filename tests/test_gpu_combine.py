@@ -18,8 +18,8 @@ from oracle import quant as oquant
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,sample", [("ep8_256x8_h7168", None), ("ep8_2048x8_h7168", 1024),
-                                         ("ep8_2048x8_h4096", 1024)])
+@pytest.mark.parametrize("name,sample", [("ep8_256x8_h7168", None), ("ep8_2048x8_h7168", None),
+                                         ("ep8_2048x8_h4096", None)])
 def test_combine_workloads(name, sample):
     """Full-expert layout (every assignment is a row), synthetic expert
     outputs [T*k, width], top-k routing weights."""
@@ -39,9 +39,9 @@ def test_combine_workloads(name, sample):
         np.concatenate([[0, d.T - 1], np.random.default_rng(2).choice(d.T, sample, replace=False)]))
     acc, _ = ocombine.combine(Y, ref["assign_row"], wts, d.T, d.k, tokens=toks)
     got = host_u16(out[torch.from_numpy(toks).cuda()])
-    ok, rel, mx, rms = tolerance(got, acc)
-    say(f"  tokens={toks.size} rel_l2={rel:.3e} max_abs={mx:.3e} rms={rms:.3e}")
-    assert ok, (rel, mx, rms)
+    t = tolerance(got, acc)
+    say(f"  tokens={toks.size} {t}")
+    assert t.ok, str(t)
 
 
 def test_combine_identity_experts_bit_exact():
@@ -91,8 +91,8 @@ def test_combine_odd_k_vs_oracle(k):
     out = moe.combine(d, width, dev(Y.view(np.int16)), dev(ar), dev(wt))
     torch.cuda.synchronize()
     acc, _ = ocombine.combine(Y, ar, wt, T, k)
-    ok, rel, mx, rms = tolerance(host_u16(out), acc)
-    assert ok, (rel, mx, rms)
+    t = tolerance(host_u16(out), acc)
+    assert t.ok, str(t)
 
 
 def test_tiny_chain_end_to_end():
@@ -114,6 +114,6 @@ def test_tiny_chain_end_to_end():
     rq, rs = oquant.quant_dispatch(x, ref["slot_tok"])
     y32 = ogemm1.grouped_gemm1(rq, rs, ref["row_slot"], ref["expert_offsets"], wq, ws)
     acc, _ = ocombine.combine(obf16.from_f32(y32), ref["assign_row"], wts, d.T, d.k)
-    ok, rel, mx, rms = tolerance(host_u16(out), acc)
-    say(f"  chain rel_l2={rel:.3e} max_abs={mx:.3e} rms={rms:.3e}")
-    assert ok, (rel, mx, rms)
+    t = tolerance(host_u16(out), acc)
+    say(f"  chain {t}")
+    assert t.ok, str(t)

@@ -54,17 +54,17 @@ def _check(d, n, ids, x, wq, ws, sample=None):
     row_slot_compact[rows] = inv
     yref = ogemm1.grouped_gemm1(rq, rs, row_slot_compact, ref["expert_offsets"], wq, ws, rows=rows)
     got = host_u16(y[torch.from_numpy(rows).cuda()]) if rows.size else np.zeros((0, n), np.uint16)
-    ok, rel, mx, rms = tolerance(got, yref)
-    say(f"  rows={rows.size} rel_l2={rel:.3e} max_abs={mx:.3e} rms={rms:.3e}")
-    assert ok, (rel, mx, rms)
+    t = tolerance(got, yref)
+    say(f"  rows={rows.size} {t}")
+    assert t.ok, str(t)
     # rows past R untouched
     assert bool((y[R:] == Y_POISON).all())
     return ref, y
 
 
 @pytest.mark.parametrize("name,sample", [
-    ("tiny_t64_h256_e8", None), ("ep8_256x8_h7168", None), ("ep8_2048x8_h7168", 512),
-    ("ep8_2048x8_h4096", 512), ("ep8_8192x8_h7168_zipf", 384),
+    ("tiny_t64_h256_e8", None), ("ep8_256x8_h7168", None), ("ep8_2048x8_h7168", None),
+    ("ep8_2048x8_h4096", None), ("ep8_8192x8_h7168_zipf", 384),
 ])
 def test_gemm1_workloads(name, sample):
     require_gpu()

@@ -37,8 +37,8 @@ def _compare(ref_lay, q, qs, x_bits, slots):
 
 
 @pytest.mark.parametrize("name,sample", [
-    ("tiny_t64_h256_e8", None), ("ep8_256x8_h7168", None), ("ep8_2048x8_h7168", 768),
-    ("ep8_2048x8_h4096", 768), ("ep8_8192x8_h7168_zipf", 512),
+    ("tiny_t64_h256_e8", None), ("ep8_256x8_h7168", None), ("ep8_2048x8_h7168", None),
+    ("ep8_2048x8_h4096", None), ("ep8_8192x8_h7168_zipf", 2048),
 ])
 def test_quant_workloads(name, sample):
     require_gpu()

@@ -148,9 +148,9 @@ def _check_gemm2_mx(d, I, ids, wts, q2, s2, w2, w2s, sample=None, seed=23):
     yref = ostage2.grouped_gemm2_mx(q2[rows], s2[rows], ref["expert_offsets"], ref["row_assign"], wts, w2, w2s,
                                     rows=rows, q_index=np.arange(rows.size))
     got = host_u16(y2[torch.from_numpy(rows).cuda()]) if rows.size else np.zeros((0, d.H), np.uint16)
-    ok, rel, mxe, rms = tolerance(got, yref)
-    say(f"  gemm2_mx rows={rows.size} rel_l2={rel:.3e} max_abs={mxe:.3e} rms={rms:.3e}")
-    assert ok, (rel, mxe, rms)
+    t = tolerance(got, yref)
+    say(f"  gemm2_mx rows={rows.size} {t}")
+    assert t.ok, str(t)
     assert bool((y2[R:] == Y_POISON).all())
 
 
