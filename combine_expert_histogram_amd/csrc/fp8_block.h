@@ -2,27 +2,36 @@
 // fp32 scale per 128-element block (the landed tokens' rows, and stage2's
 // silu(gate) * up rows): a block is held by 8 adjacent lanes, 16 values each.
 //
-// Bit-exactness: the definition is e4m3(x / s), s = amax / 448, with IEEE
-// divisions.  Neither division is done on the fast path:
+// Bit-exactness: the definition is e4m3(fl32(x / s)), s = fl32(amax / 448),
+// IEEE divisions, round to nearest even.  Neither division is done on the
+// fast path:
 //  * s: s0 = amax * c with c = fl(1/448); the residual amax - 448 * s0 is exact
 //    in fp32 (one fma), and s = fma(residual, c, s0) is the correctly rounded
 //    quotient.  Checked exhaustively against the IEEE quotient for every fp32
 //    mantissa of a binade (and exactly, in rational arithmetic, for every
 //    bf16 amax); the result scales by powers of two, so it holds for every
-//    amax >= 2^-100, where no intermediate is subnormal.  Smaller maxima take
-//    the IEEE division.
-//  * x / s is bracketed instead: r = 1/s to within a few 2^-24 (v_rcp_f32 and
-//    one Newton step), r_hi = r * (1 + 2^-20) and r_lo = r * (1 - 2^-20)
-//    satisfy r_lo <= 1/s <= r_hi, so x * r_lo <= x / s <= x * r_hi for x >= 0
-//    (reversed for x < 0), and rounding to fp32 keeps that order.  The
-//    hardware conversion (v_cvt_pk_fp8_f32: OCP e4m3, round to nearest even,
-//    subnormal results included) is monotone, so when the codes of x * r_lo
-//    and x * r_hi agree, the code of the IEEE quotient is the same one.  They
-//    differ only when a rounding boundary of e4m3 lies in the 2^-19-wide
-//    bracket (about one element in 5 * 10^4); a lane holding such an element
-//    redoes its 16 values with the IEEE division.  Every |x * r_hi| is below
-//    448 * (1 + 2^-19), far under the 464 rounding boundary, so no saturation
-//    case arises.
+//    amax >= 2^-100, where no intermediate is subnormal.  Smaller, infinite
+//    and NaN maxima take the IEEE divisions.
+//  * fl32(x / s) is computed as fl32(fl64(x * R)), R ~ 1/s in fp64: r = v_rcp_f32
+//    with one fp32 Newton step (relative error about 2^-23), then two fp64
+//    Newton steps, leaving |R s - 1| below about 2^-52, so fl64(x * R) is within
+//    2^-51 (relative) of x / s.  That is close enough, for any fp32 x, where
+//    the quotient is a normal fp32 number: a rounding midpoint M there has a
+//    25-bit odd significand m1 and s a 24-bit one m2, so x = M s would make m1
+//    divide x's significand, which is impossible, and near equality x - M s is
+//    a nonzero multiple of the last bit of M s (x's exponent must be at least
+//    22 above it for the magnitudes to match), so |x/s - M| >= 2^-49 |M|.  x / s
+//    and its fp64 approximation therefore lie on the same side of every such
+//    midpoint and round to the same fp32 value.  Quotients below 2^-126 may
+//    differ from the IEEE one in their last place, but every magnitude below
+//    2^-10 encodes to a zero of x's sign, so the codes agree.  The hardware
+//    conversion (v_cvt_pk_fp8_f32: OCP e4m3, round to nearest even, subnormal
+//    results included) then gives the code.  |fl32(x / s)| <= 448 (1 + 2^-22),
+//    far under the 464 rounding boundary, so no saturation case arises.
+//    Inputs with few significant bits (bf16 activations) put x / s within
+//    2^-19 of an e4m3 midpoint for about one element in 200, so a cheaper
+//    fp32 bracket with an IEEE fallback would take the fallback in nine passes
+//    of ten.
 #pragma once
 
 #include "common.h"
@@ -59,38 +68,32 @@ __device__ __forceinline__ float div448(float amax) {
 }
 
 // Codes of this lane's 16 values of a block whose |max| over all its 128
-// values is amax (the same in the block's 8 lanes): out[i] holds the codes of
-// x[4i .. 4i+3], byte j = x[4i+j].  Returns the block's scale s = amax / 448
-// (0 for an all-zero block, whose codes are 0).
+// values is amax (the same in the block's 8 lanes; a magnitude, never -0):
+// out[i] holds the codes of x[4i .. 4i+3], byte j = x[4i+j].  Returns the
+// block's scale s = amax / 448 (+0 for an all-zero block, whose codes are 0).
 __device__ __forceinline__ float encode_block16(const float (&xv)[16], float amax, uint32_t (&out)[4]) {
-    const bool zero = amax == 0.0f;
-    // maxima below 2^-100 (rare: the workloads never produce them) take the IEEE
-    // divisions throughout
-    const bool tiny = !(amax >= 0x1p-100f);
-    float s;
-    if (__builtin_expect(tiny, 0)) s = amax / 448.0f;
-    else s = div448(amax);
-    const float r0 = __builtin_amdgcn_rcpf(s);
-    const float r = fmaf(r0, fmaf(-s, r0, 1.0f), r0);
-    const float r_hi = __fmul_rn(r, 1.0f + 0x1p-20f), r_lo = __fmul_rn(r, 1.0f - 0x1p-20f);
-    bool slow = tiny;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t hi = cvt4(__fmul_rn(xv[4 * i], r_hi), __fmul_rn(xv[4 * i + 1], r_hi),
-                                 __fmul_rn(xv[4 * i + 2], r_hi), __fmul_rn(xv[4 * i + 3], r_hi));
-        const uint32_t lo = cvt4(__fmul_rn(xv[4 * i], r_lo), __fmul_rn(xv[4 * i + 1], r_lo),
-                                 __fmul_rn(xv[4 * i + 2], r_lo), __fmul_rn(xv[4 * i + 3], r_lo));
-        slow |= hi != lo;
-        out[i] = hi;
-    }
-    if (slow && !zero) {
+    // maxima below 2^-100 (rare: the workloads never produce them), zero,
+    // infinity and NaN take the IEEE divisions
+    if (__builtin_expect(!(amax >= 0x1p-100f && amax <= 0x1.fffffep127f), 0)) {
+        const float s = amax / 448.0f;
+        const bool zero = amax == 0.0f;                 // codes 0 (x / 0 would give NaN)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            out[i] = cvt4(xv[4 * i] / s, xv[4 * i + 1] / s, xv[4 * i + 2] / s, xv[4 * i + 3] / s);
+            out[i] = zero ? 0u : cvt4(xv[4 * i] / s, xv[4 * i + 1] / s, xv[4 * i + 2] / s, xv[4 * i + 3] / s);
+        return s;
     }
+    const float s = div448(amax);
+    const float r0 = __builtin_amdgcn_rcpf(s);
+    const float r = fmaf(r0, fmaf(-s, r0, 1.0f), r0);
+    const double sd = (double)s;
+    double R = (double)r;
+    R = fma(R, fma(-sd, R, 1.0), R);
+    R = fma(R, fma(-sd, R, 1.0), R);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = zero ? 0u : out[i];
-    return zero ? 0.0f : s;
+    for (int i = 0; i < 4; ++i)
+        out[i] = cvt4((float)((double)xv[4 * i] * R), (float)((double)xv[4 * i + 1] * R),
+                      (float)((double)xv[4 * i + 2] * R), (float)((double)xv[4 * i + 3] * R));
+    return s;
 }
 
 // MX (e8m0) group exponent: E = ceil(log2(t)), t = amax / 448 (IEEE fp32

@@ -137,3 +137,30 @@ def test_quant_ragged_hidden():
     rng = np.random.default_rng(6)
     x = (rng.standard_normal((300, 1152)) * np.exp2(rng.uniform(-8, 8, (300, 1)))).astype(np.float32)
     _quant_rows(obf16.from_f32(x))
+
+
+def test_quant_out_of_range_tokens_leave_rows_unwritten():
+    """Slot tokens outside [0, T) (the layout never produces them) are read as
+    row 0 and their slot rows left unwritten; every other row is unchanged
+    (H = 1152: the last pass holds one block, so lanes past it are live)."""
+    require_gpu()
+    rng = np.random.default_rng(8)
+    T, H = 300, 1152
+    x = obf16.from_f32((rng.standard_normal((T, H)) * np.exp2(rng.uniform(-8, 8, (T, 1)))).astype(np.float32))
+    d = moe.Dims(S=1, Ts=T, k=1, E=1, e0=0, L=1, H=H)
+    ids = np.zeros((T, 1), np.int32)
+    ref_lay = olayout.route_layout(ids, 1, T, 1, 0, 1)
+    lay = moe.route_layout(d, dev(ids.reshape(-1)), poisoned_layout(d))
+    bad = [0, 5, 131, T - 1]
+    lay["slot_tok"][bad[0]] = -1
+    lay["slot_tok"][bad[1]] = T
+    lay["slot_tok"][bad[2]] = T + 1000
+    lay["slot_tok"][bad[3]] = -(1 << 30)
+    q = torch.full((T, H), 0xA5, dtype=torch.uint8, device="cuda")
+    qs = torch.full((T, H // 128), -7.0, dtype=torch.float32, device="cuda")
+    moe.quant_dispatch(d, dev(x.view(np.int16)), lay, q, qs)
+    torch.cuda.synchronize()
+    good = np.setdiff1d(np.arange(T), bad)
+    _compare(ref_lay, q, qs, x, good)
+    for u in bad:
+        assert (q[u] == 0xA5).all() and (qs[u] == -7.0).all(), f"slot {u} written"
