@@ -1,7 +1,10 @@
-"""Builds libmoe_hotpath.so (gfx950) in-tree with hipcc, and libmoe_ceiling.so,
-the benchmark's MFMA-rate probe (not part of the hot path's C ABI).
+"""Builds libmoe_hotpath.so (gfx950) in-tree with hipcc; libmoe_ceiling.so,
+the benchmark's read-stream and MFMA-rate probes (not part of the hot path's C
+ABI); and libmoe_hotpath_trace.so, the same sources with the clock-stamp trace
+compiled in (MOE_TRACE=1, csrc/trace.h), which `python -m
+combine_expert_histogram_amd.trace` loads.
 
-Usage: python -m combine_expert_histogram_amd.build
+Usage: python -m combine_expert_histogram_amd.build [-v] [--no-trace]
 """
 from __future__ import annotations
 
@@ -16,6 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_hotpath.so")
 SOURCES = ["api.hip", "layout.hip", "quant.hip", "gemm1.hip", "stage2.hip", "combine.hip"]
+TRACE_LIB = os.path.join(PKG, "libmoe_hotpath_trace.so")
 CEILING_LIB = os.path.join(PKG, "libmoe_ceiling.so")
 CEILING_SOURCES = ["ceiling.hip"]
 ARCH = "gfx950"
@@ -40,10 +44,10 @@ def flags() -> list[str]:
     ]
 
 
-def _link(sources: list[str], out: str, verbose: bool) -> str:
+def _link(sources: list[str], out: str, verbose: bool, extra: tuple[str, ...] = ()) -> str:
     srcs = [os.path.join(CSRC, s) for s in sources]
     tmp = out + ".tmp"
-    cmd = [hipcc(), *flags(), *srcs, "-o", tmp]
+    cmd = [hipcc(), *flags(), *extra, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,10 +57,12 @@ def _link(sources: list[str], out: str, verbose: bool) -> str:
     return out
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, trace: bool = True) -> str:
     _link(CEILING_SOURCES, CEILING_LIB, verbose)
+    if trace:
+        _link(SOURCES, TRACE_LIB, verbose, ("-DMOE_TRACE=1",))
     return _link(SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, trace="--no-trace" not in sys.argv))

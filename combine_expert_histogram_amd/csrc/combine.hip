@@ -21,6 +21,7 @@ __global__ void __launch_bounds__(kThreads)
 combine_kernel(const uint16_t* __restrict__ y, int64_t y_rows, const int32_t* __restrict__ assign_row,
                const float* __restrict__ topk_w, uint16_t* __restrict__ out, int width, int k,
                int col_blocks) {
+    MOE_TRACE_T0(tr0);
     const int64_t g = blockIdx.x / col_blocks;
     const int cb = blockIdx.x - (int)(g * col_blocks);
     const int c8 = cb * kThreads + threadIdx.x;         // group of 8 columns
@@ -60,6 +61,7 @@ combine_kernel(const uint16_t* __restrict__ y, int64_t y_rows, const int32_t* __
     o.z = moe::f32_to_bf16_rne(acc[4]) | (moe::f32_to_bf16_rne(acc[5]) << 16);
     o.w = moe::f32_to_bf16_rne(acc[6]) | (moe::f32_to_bf16_rne(acc[7]) << 16);
     __builtin_nontemporal_store(o, reinterpret_cast<moe::u32x4*>(out + g * width) + c8);
+    if (threadIdx.x == 0) MOE_TRACE_PUT(moe::kTrCombine, blockIdx.x, 0, 0, tr0);
 }
 
 }  // namespace

@@ -8,6 +8,7 @@
 #include <algorithm>
 
 #include "moe_hotpath.h"
+#include "trace.h"
 
 #define MOE_WAVE 64
 

@@ -144,6 +144,7 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
                      const uint8_t* __restrict__ w, const void* __restrict__ w_scale_v,
                      uint16_t* __restrict__ y, int N, int H, int64_t T, int64_t scale_ld,
                      const float* __restrict__ wtab) {
+    MOE_TRACE_T0(tr0);
     // fp32 path: one float per (expert, 128 columns, K block), [L, N/128, H/128];
     // MX path: packed e8m0 codes per (expert, K block, column), [L, H/128, N]
     const float* w_scale = static_cast<const float*>(w_scale_v);
@@ -274,6 +275,7 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
             if (g + NSTAGE - 1 < nsteps) issue(g + NSTAGE - 1);
         }
         __builtin_amdgcn_s_waitcnt(wait_vm(0));
+        if (lw == 0 && lane == 0) MOE_TRACE_PUT(moe::kTrGemmLoader, blockIdx.x, 0, 0, tr0);
         return;
     }
 
@@ -285,6 +287,7 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
     const int wm = wave / WN, wn = wave % WN;
     int g = 0;
     for (int it = 0; it < ntiles; ++it) {
+        MOE_TRACE_T0(tr_tile);
         const int4 td = tiles[1 + it * G + my];
         const int e = td.x, r0 = td.z, nvalid = td.w & 511;
         const int n0 = td.y * BN;
@@ -473,7 +476,9 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
                 }
             }
         }
+        if (wave == 0 && lane == 0) MOE_TRACE_PUT(moe::kTrGemmTile, (uint32_t)(it * G + my), (uint32_t)(it * G + my), (uint32_t)it, tr_tile);
     }
+    if (wave == 0 && lane == 0) MOE_TRACE_PUT(moe::kTrGemmCompute, blockIdx.x, 0, 0, tr0);
 }
 
 // Pre-pass, one launch:
@@ -503,6 +508,7 @@ gemm1_prep_kernel(const uint32_t* __restrict__ q_scale, const int32_t* __restric
                   const int32_t* __restrict__ expert_offsets, int L, int KB, int NT, int64_t T,
                   int64_t rows_cap, int64_t scale_ld, uint32_t* __restrict__ out, int4* __restrict__ tiles,
                   int64_t tiles_cap) {
+    MOE_TRACE_T0(tr0);
     if (blockIdx.x == 0) {
         __shared__ int eoff[kMaxL + 1];
         __shared__ int tstart[kMaxL + 1];
@@ -555,6 +561,7 @@ gemm1_prep_kernel(const uint32_t* __restrict__ q_scale, const int32_t* __restric
             tiles[1 + t] = int4{e, nt, r0, nvalid | (mtile << 9)};
         }
         if (tid == 0) tiles[0] = int4{total, 0, 0, 0};
+        if (tid == 0) MOE_TRACE_PUT(moe::kTrGemmPrep, blockIdx.x, 0, 0, tr0);
         return;
     }
     int64_t R = expert_offsets[L];
@@ -588,6 +595,7 @@ gemm1_prep_kernel(const uint32_t* __restrict__ q_scale, const int32_t* __restric
         for (int i = 0; i < kPrepKb; ++i)
             if (k0 + i < KB) out[(int64_t)(k0 + i) * scale_ld + r] = v[i];
     }
+    if (threadIdx.x == 0) MOE_TRACE_PUT(moe::kTrGemmPrep, blockIdx.x, 1, 0, tr0);
 }
 
 // Rows of the table: every row a tile can name (rows_cap plus one tile of the

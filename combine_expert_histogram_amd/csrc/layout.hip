@@ -91,6 +91,7 @@ __device__ __forceinline__ void wave_sync_lds() {
 __global__ void __launch_bounds__(kBlock)
 layout_count_kernel(const int32_t* __restrict__ ids, int64_t T, int k, int e0, int L, int CB,
                     int NCp, int32_t* __restrict__ hist, int32_t* __restrict__ landed) {
+    MOE_TRACE_T0(tr0);
     extern __shared__ __align__(16) unsigned char smem[];
     int* cnt = reinterpret_cast<int*>(smem);
     int* red = cnt + L;                                   // 16 ints
@@ -131,6 +132,7 @@ layout_count_kernel(const int32_t* __restrict__ ids, int64_t T, int k, int e0, i
     for (int i = tid; i < L; i += kBlock) hist[(int64_t)i * NCp + c] = cnt[i];
     __syncthreads();
     if (tid == 0) landed[c] = red[0] + red[1] + red[2] + red[3];
+    if (tid == 0) MOE_TRACE_PUT(moe::kTrLayoutCount, blockIdx.x, 0, 0, tr0);
 }
 
 // ------------------------------------------------------------------ place
@@ -142,6 +144,7 @@ layout_place_kernel(const int32_t* __restrict__ ids, int64_t T, int k, int e0, i
                     int32_t* __restrict__ row_assign, int32_t* __restrict__ assign_row,
                     int32_t* __restrict__ tok_slot, int32_t* __restrict__ slot_tok,
                     int32_t* __restrict__ src_slot_offsets, int32_t* __restrict__ totals) {
+    MOE_TRACE_T0(tr0);
     extern __shared__ __align__(16) unsigned char smem[];
     const PlaceLds lo = place_lds(L, CB);
     const int tid = threadIdx.x;
@@ -373,6 +376,7 @@ layout_place_kernel(const int32_t* __restrict__ ids, int64_t T, int k, int e0, i
         const int64_t a = a0 + p * MOE_WAVE + lane;
         place_one(a, a < a1 ? ids[a] : 0);
     }
+    if (tid == 0) MOE_TRACE_PUT(moe::kTrLayoutPlace, blockIdx.x, 0, 0, tr0);
 }
 
 // Validates the layout call's arguments and sizes its plan; no HIP call.

@@ -36,6 +36,7 @@ __global__ void __launch_bounds__(kBlock)
 quant_dispatch_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ slot_tok,
                       const int32_t* __restrict__ totals, int64_t T, int H,
                       uint8_t* __restrict__ q, float* __restrict__ q_scale) {
+    MOE_TRACE_T0(tr0);
     const int64_t U = min((int64_t)totals[1], T);     // slots_cap = T
     const int lane = threadIdx.x % MOE_WAVE;
     const int sub = lane & 7;                    // 16-element piece within a block
@@ -91,6 +92,7 @@ quant_dispatch_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict_
             }
         }
     }
+    if (threadIdx.x % MOE_WAVE == 0) MOE_TRACE_PUT(moe::kTrQuant, blockIdx.x * kWaves + threadIdx.x / MOE_WAVE, threadIdx.x / MOE_WAVE, 0, tr0);
 }
 
 // MX-style variant ("Where we stand": e8m0 block scales; commit
@@ -107,6 +109,7 @@ __global__ void __launch_bounds__(kBlock)
 quant_dispatch_mx_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ slot_tok,
                          const int32_t* __restrict__ totals, int64_t T, int H,
                          uint8_t* __restrict__ q, uint32_t* __restrict__ q_scale) {
+    MOE_TRACE_T0(tr0);
     const int64_t U = min((int64_t)totals[1], T);
     const int lane = threadIdx.x % MOE_WAVE;
     const int sub = lane & 7;
@@ -167,6 +170,7 @@ quant_dispatch_mx_kernel(const uint16_t* __restrict__ x, const int32_t* __restri
             }
         }
     }
+    if (threadIdx.x % MOE_WAVE == 0) MOE_TRACE_PUT(moe::kTrQuantMx, blockIdx.x * kWaves + threadIdx.x / MOE_WAVE, threadIdx.x / MOE_WAVE, 0, tr0);
 }
 
 }  // namespace

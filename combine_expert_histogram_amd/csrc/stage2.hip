@@ -37,6 +37,7 @@ template <bool MX>
 __global__ void __launch_bounds__(kBlock)
 silu_mul_quant_kernel(const uint16_t* __restrict__ y1, const int32_t* __restrict__ totals, int64_t rows_cap,
                       int I, uint8_t* __restrict__ q, void* __restrict__ q_scale_v) {
+    MOE_TRACE_T0(tr0);
     const int64_t R = min((int64_t)totals[0], rows_cap);
     const int lane = threadIdx.x % MOE_WAVE;
     const int sub = lane & 7;
@@ -93,6 +94,7 @@ silu_mul_quant_kernel(const uint16_t* __restrict__ y1, const int32_t* __restrict
             }
         }
     }
+    if (threadIdx.x % MOE_WAVE == 0) MOE_TRACE_PUT(moe::kTrAct, blockIdx.x * kWaves + threadIdx.x / MOE_WAVE, threadIdx.x / MOE_WAVE, 0, tr0);
 }
 
 template <bool MX>
