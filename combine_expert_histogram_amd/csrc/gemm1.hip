@@ -76,6 +76,14 @@ constexpr int kXcds = 8;
 constexpr int kMinBM = 128;   // tile descriptors are sized for the smallest row tile
 constexpr int kPrepKb = 8;    // K blocks per row-scale gather work item
 constexpr int kPrepWgPerCu = 4;   // gather workgroups of the pre-pass per CU
+// schedule slots past the tile count (the balanced schedule's last round can
+// leave up to one grid's worth of idle slots); also the largest main grid
+constexpr int kMaxGrid = 1024;
+// the cost-balanced tile schedule is used for K loops of at least this many
+// steps (GEMM1's 56: -5 %); with short tiles (GEMM2's 16 steps) the drift it
+// introduces between the workgroups that share a weight slab cost more L2
+// reuse than it saved (+10 %), so those keep the plain round-robin
+constexpr int kBalanceMinKb = 32;
 
 #define GPTR(p) ((const void __attribute__((address_space(1)))*)(p))
 #define LPTR(p) ((void __attribute__((address_space(3)))*)(p))
@@ -176,7 +184,6 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
     const int b = blockIdx.x;
     const int my = (b % kXcds) * (G / kXcds) + b / kXcds;   // G is a multiple of 8
     const int ntiles = total > my ? (total - my + G - 1) / G : 0;
-    const int nsteps = ntiles * KB;
 
     if (wave >= C::kCompute) {
         // ---------------- loader wavefronts ----------------
@@ -197,9 +204,12 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
         int ncols = BN;
         const uint32_t* wsc_mx = w_scale_mx;
         const float* wsc_f = w_scale;
+        // steps of this workgroup: its slots' tiles, up to the first idle slot
+        int nsteps = ntiles * KB;
         auto setup = [&](int it) __attribute__((always_inline)) {
             const int4 td = tiles[1 + it * G + my];
             const int e = td.x, r0 = td.z, nvalid = td.w & 511;
+            if (nvalid == 0) return false;
             const int n0 = td.y * BN;
             ncols = min(BN, N - n0);
             if (MX) {
@@ -227,13 +237,20 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
             }
             wexp = w + ((int64_t)e * N + n0) * H;
             srow = row_scale + r0 + lw * 64;
+            return true;
         };
         const uint32_t b_lane0 = (uint32_t)lrow * (uint32_t)H + kchunk(gchunk) * 16;
         const uint32_t b_lane1 = (uint32_t)lrow * (uint32_t)H + kchunk(gchunk ^ 1) * 16;
         const uint32_t s_lane = (uint32_t)lane * 4u;
         auto issue = [&](int s) __attribute__((always_inline)) {
             const int it = s / KB, kb = s - it * KB;
-            if (it != cur) { setup(it); cur = it; }
+            if (it != cur) {
+                if (!setup(it)) {                 // an idle slot: this workgroup's tiles end here
+                    nsteps = s;
+                    return;
+                }
+                cur = it;
+            }
             uint8_t* base = ring + (s % NSTAGE) * STAGE;
 #pragma unroll
             for (int i = 0; i < A_LOADS; ++i)
@@ -290,6 +307,7 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
         MOE_TRACE_T0(tr_tile);
         const int4 td = tiles[1 + it * G + my];
         const int e = td.x, r0 = td.z, nvalid = td.w & 511;
+        if (nvalid == 0) break;                   // an idle slot: this workgroup's tiles end here
         const int n0 = td.y * BN;
         const int ncols = min(BN, N - n0);
         const bool active = wm * RW < nvalid && wn * CW < ncols;
@@ -496,10 +514,11 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
 //    weight goes to wtab[r] for the main kernel's epilogue.
 //  * tile descriptors (workgroup 0, dispatched first, so its serial work runs
 //    beside the gather instead of after the dispatch of every gather
-//    workgroup): per local expert ceil(count / BM)
-//    row tiles times NT column tiles, experts in order, column tiles outer and
-//    row tiles inner; tiles[0].x = number of tiles, tiles[1 + t] =
-//    {expert, column tile, first row, valid rows | row tile << 9}.
+//    workgroup): per local expert ceil(count / BM) row tiles times NT column
+//    tiles, {expert, column tile, first row, valid rows | row tile << 9}, in
+//    the main kernel's schedule order (slot it * G + my is tile it of
+//    workgroup my; zero valid rows: an idle slot); tiles[0].x = number of
+//    slots, tiles[1 + slot] = the descriptors.
 template <int BM>
 __global__ void __launch_bounds__(256)
 gemm1_prep_kernel(const uint32_t* __restrict__ q_scale, const int32_t* __restrict__ row_slot,
@@ -507,7 +526,7 @@ gemm1_prep_kernel(const uint32_t* __restrict__ q_scale, const int32_t* __restric
                   float* __restrict__ wtab,
                   const int32_t* __restrict__ expert_offsets, int L, int KB, int NT, int64_t T,
                   int64_t rows_cap, int64_t scale_ld, uint32_t* __restrict__ out, int4* __restrict__ tiles,
-                  int64_t tiles_cap) {
+                  int64_t tiles_cap, int G) {
     MOE_TRACE_T0(tr0);
     if (blockIdx.x == 0) {
         __shared__ int eoff[kMaxL + 1];
@@ -546,7 +565,9 @@ gemm1_prep_kernel(const uint32_t* __restrict__ q_scale, const int32_t* __restric
         // offsets from the layout give at most rows_cap / BM + L row tiles; the clamp
         // only keeps malformed offsets inside the descriptor array
         const int total = (int)min((int64_t)tstart[L], tiles_cap);
-        for (int t = tid; t < total; t += 256) {
+        // tile t of the natural order: experts in order, column tiles outer, row
+        // tiles inner (the row tiles that share a weight slab adjacent)
+        auto natural = [&](int t) __attribute__((always_inline)) {
             int lo = 0, hi = L - 1;
             while (lo < hi) {
                 const int mid = (lo + hi + 1) >> 1;
@@ -558,9 +579,59 @@ gemm1_prep_kernel(const uint32_t* __restrict__ q_scale, const int32_t* __restric
             const int nt = local / mt, mtile = local - nt * mt;
             const int r0 = eoff[e] + mtile * BM;
             const int nvalid = min(BM, eoff[e + 1] - r0);
-            tiles[1 + t] = int4{e, nt, r0, nvalid | (mtile << 9)};
+            return int4{e, nt, r0, nvalid | (mtile << 9)};
+        };
+        const int nx = G / kXcds;                  // workgroups per XCD
+        if (KB < kBalanceMinKb || G % kXcds != 0 || nx < 1 || nx > MOE_WAVE) {
+            // plain round-robin over the natural order
+            for (int t = tid; t < total; t += 256) tiles[1 + t] = natural(t);
+            if (tid == 0) tiles[0] = int4{total, 0, 0, 0};
+        } else {
+            // Balanced static schedule.  Round r gives XCD x the natural tiles
+            // [r * G + x * nx, + nx), as the plain round-robin does, so the row tiles
+            // that share a weight slab run in one round on one XCD (together in its
+            // L2).  Within the round they go to the XCD's workgroups by cost: the
+            // costliest tile to the workgroup with the least work so far.  Cost: a
+            // full tile 1000, a partial one 700 + 300 * rows / BM (a tile streams its
+            // whole weight slab whatever its rows).  Slot (round r, workgroup (x, j))
+            // is descriptor 1 + r * G + x * nx + j; a round with fewer tiles than
+            // workgroups (only the last) leaves idle slots (zero rows), which end
+            // their workgroups.  Wavefront wv plans XCDs wv and wv + 4.
+            __shared__ int rank_tile[256 / MOE_WAVE][MOE_WAVE];
+            const int R = (total + G - 1) / G;                              // rounds
+            auto cost = [&](const int4 dsc) __attribute__((always_inline)) {
+                return 700 + (300 * (dsc.w & 511)) / BM;
+            };
+            for (int x = wv; x < kXcds; x += 256 / MOE_WAVE) {
+                int acc = 0;                                       // lane j < nx: workgroup j's work so far
+                for (int r = 0; r < R; ++r) {
+                    const int c0 = r * G + x * nx;
+                    const int m = max(0, min(nx, total - c0));     // tiles of this round
+                    const int4 d = lane < m ? natural(c0 + lane) : int4{0, 0, 0, 0};
+                    const int tc = lane < m ? cost(d) : -1;
+                    // tiles by cost, descending; workgroups by work, ascending (ties: lower lane first)
+                    int trank = 0, wrank = 0;
+                    for (int k = 0; k < nx; ++k) {
+                        const int ck = __shfl(tc, k, MOE_WAVE), ak = __shfl(acc, k, MOE_WAVE);
+                        trank += (ck > tc || (ck == tc && k < lane)) ? 1 : 0;
+                        wrank += (ak < acc || (ak == acc && k < lane)) ? 1 : 0;
+                    }
+                    if (lane < nx) rank_tile[wv][trank] = lane;
+                    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    const int tl = lane < nx ? rank_tile[wv][wrank] : 0;   // the lane holding this workgroup's tile
+                    const int4 mine = int4{__shfl(d.x, tl, MOE_WAVE), __shfl(d.y, tl, MOE_WAVE),
+                                           __shfl(d.z, tl, MOE_WAVE), __shfl(d.w, tl, MOE_WAVE)};
+                    if (lane < nx) {
+                        tiles[1 + r * G + x * nx + lane] = tl < m ? mine : int4{0, 0, 0, 0};
+                        acc += tl < m ? cost(mine) : 0;
+                    }
+                    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                }
+            }
+            if (tid == 0) tiles[0] = int4{R * G, 0, 0, 0};
         }
-        if (tid == 0) tiles[0] = int4{total, 0, 0, 0};
         if (tid == 0) MOE_TRACE_PUT(moe::kTrGemmPrep, blockIdx.x, 0, 0, tr0);
         return;
     }
@@ -616,7 +687,8 @@ int cu_count() {
 using TileCfg = Cfg<128, 2, 4, 4, 3, 1>;
 static_assert(TileCfg::BM <= kMaxBM, "scale table padding covers one tile");
 
-// Workspace: the row-scale table, then the tile descriptors (16 B each).
+// Workspace: the row-scale table, then the tile descriptors (16 B each; the
+// schedule may hold up to kMaxGrid idle slots beyond the tiles).
 struct WsLayout {
     int64_t scale_ld, table_bytes, tiles_cap, wtab_off, bytes;
 };
@@ -627,8 +699,8 @@ WsLayout ws_layout(int64_t rows_cap, int64_t KB, int64_t n, int64_t L, bool row_
     l.scale_ld = scale_ld_of(rows_cap);
     l.table_bytes = (KB * l.scale_ld * 4 + 255) & ~int64_t(255);
     l.tiles_cap = (rows_cap / kMinBM + L) * ((n + BN - 1) / BN);
-    l.wtab_off = (l.table_bytes + (1 + l.tiles_cap) * 16 + 255) & ~int64_t(255);
-    l.bytes = row_weights ? l.wtab_off + rows_cap * 4 : l.table_bytes + (1 + l.tiles_cap) * 16;
+    l.wtab_off = (l.table_bytes + (1 + l.tiles_cap + kMaxGrid) * 16 + 255) & ~int64_t(255);
+    l.bytes = row_weights ? l.wtab_off + rows_cap * 4 : l.table_bytes + (1 + l.tiles_cap + kMaxGrid) * 16;
     return l;
 }
 
@@ -674,12 +746,13 @@ moe_status run_gemm(const moe::Dims& d, int64_t a_rows, int64_t kdim, int64_t n,
     const int64_t KG = (KB + kPrepKb - 1) / kPrepKb;
     const int pgrid = (int)std::min<int64_t>((rows_cap * KG + 255) / 256, kPrepWgPerCu * (int64_t)cus) + 1;
     using C = TileCfg;
+    const int grid = ((cus + kXcds - 1) / kXcds) * kXcds;
+    if (grid > kMaxGrid) return MOE_ERR_UNSUPPORTED;
     hipLaunchKernelGGL((gemm1_prep_kernel<C::BM>), dim3(pgrid), dim3(256), 0, stream, q_scale,
                        DIRECT ? nullptr : row_slot, row_assign, topk_w, rows_cap, wtab, expert_offsets, (int)d.L,
-                       (int)KB, NT, a_rows, rows_cap, wl.scale_ld, row_scale, tiles, wl.tiles_cap);
+                       (int)KB, NT, a_rows, rows_cap, wl.scale_ld, row_scale, tiles, wl.tiles_cap, grid);
     moe_status st;
     if ((st = moe::launch_status()) != MOE_OK) return st;
-    const int grid = ((cus + kXcds - 1) / kXcds) * kXcds;
     hipLaunchKernelGGL((grouped_gemm1_kernel<C, MX, DIRECT>), dim3(grid), dim3(C::kThreads), 0,
                        stream, q_e4m3, row_scale, tiles, row_slot, w_e4m3, w_scale, y_bf16, (int)n, (int)kdim,
                        a_rows, wl.scale_ld, wtab);

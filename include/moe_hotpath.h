@@ -159,7 +159,8 @@ moe_status moe_quant_dispatch(const moe_dims* dims, const uint16_t* x_bf16,
 /* Workspace bytes moe_grouped_gemm1 needs (host-only): a K-block-major table of
  * the rows' activation scales, (H/128) x (rows_cap + 256, rounded up to 64) floats
  * (padded to 256 B), then 16 B tile descriptors, (1 + (rows_cap/128 + L) *
- * ceil(n/256)) of them.  Both are rewritten by every call. */
+ * ceil(n/256) + 1024) of them (the tile schedule's slots, idle ones
+ * included).  Both are rewritten by every call. */
 moe_status moe_grouped_gemm1_workspace(const moe_dims* dims, int32_t n, size_t* bytes);
 
 /*
@@ -267,8 +268,9 @@ moe_status moe_silu_mul_quant(const moe_dims* dims, int32_t inter, const uint16_
 
 /* Workspace bytes moe_grouped_gemm2 and moe_grouped_gemm2_mx need (host-only):
  * the K-block-major row scale table, (inter/128) x (rows_cap + 256, rounded up
- * to 64) words (padded to 256 B), then (1 + (rows_cap/128 + L) * ceil(H/256))
- * 16 B tile descriptors, then (from a 256 B boundary) one float per row. */
+ * to 64) words (padded to 256 B), then (1 + (rows_cap/128 + L) * ceil(H/256) +
+ * 1024) 16 B tile descriptors (as GEMM1's), then (from a 256 B boundary) one
+ * float per row. */
 moe_status moe_grouped_gemm2_workspace(const moe_dims* dims, int32_t inter, size_t* bytes);
 
 /*

@@ -55,7 +55,7 @@ def test_capacity_and_workspace(L):
     # the row-scale table (H/128 K blocks x (rows_cap + one 256-row tile, 64-aligned) floats,
     # 256 B aligned), then 16 B tile descriptors: one count + (rows_cap/128 + L) x (n/256)
     table = (56 * ((16384 * 8 + 256 + 63) // 64 * 64) * 4 + 255) // 256 * 256
-    assert b.moe_grouped_gemm1_workspace(d, 4096) == table + (1 + (16384 * 8 // 128 + 32) * 16) * 16
+    assert b.moe_grouped_gemm1_workspace(d, 4096) == table + (1 + (16384 * 8 // 128 + 32) * 16 + 1024) * 16
     # the full-expert layout used by the combine
     assert b.moe_route_layout_workspace(b.Dims(S=8, Ts=2048, k=8, E=256, e0=0, L=256)) > 0
 
@@ -116,7 +116,7 @@ def test_stage2_and_mx_workspaces(L):
     # GEMM2: K = inter, n = H; the same table + descriptor layout as GEMM1's
     inter = 2048
     table = ((inter // 128) * ((16384 * 8 + 256 + 63) // 64 * 64) * 4 + 255) // 256 * 256
-    desc_end = table + (1 + (16384 * 8 // 128 + 32) * (7168 // 256)) * 16
+    desc_end = table + (1 + (16384 * 8 // 128 + 32) * (7168 // 256) + 1024) * 16
     # then one float per row, from a 256 B boundary
     assert b.moe_grouped_gemm2_workspace(d, inter) == (desc_end + 255) // 256 * 256 + 16384 * 8 * 4
     for bad in (0, 64, 200):

@@ -99,8 +99,8 @@ def test_traced_step_records_every_kernel_and_matches_the_product():
     g = recs["gemm1"]
     offs = out["lay"]["expert_offsets"].cpu().numpy()
     tiles = int(sum(-(-int(c) // 128) for c in np.diff(offs))) * (w.N // 256)
-    assert (g["kernel"] == 8).sum() == tiles
-    assert sorted(g["item"][g["kernel"] == 8].tolist()) == list(range(tiles))
+    slots = g["item"][g["kernel"] == 8]
+    assert slots.size == tiles and np.unique(slots).size == tiles     # one record per tile, by schedule slot
     assert (g["kernel"] == 6).sum() == (g["kernel"] == 7).sum() > 0
     # the traced library computes the same bytes
     assert torch.equal(out["lay"]["row_slot"][:R], lay_p["row_slot"][:R])
