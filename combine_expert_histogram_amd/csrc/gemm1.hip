@@ -84,6 +84,10 @@ constexpr int kMaxGrid = 1024;
 // introduces between the workgroups that share a weight slab cost more L2
 // reuse than it saved (+10 %), so those keep the plain round-robin
 constexpr int kBalanceMinKb = 32;
+// the planner's limits: 32 workgroups per XCD (a half wavefront each), and a
+// row count per tile in LDS (one byte each)
+constexpr int kPlanMaxNx = 32;
+constexpr int kPlanMaxTiles = 16384;
 
 #define GPTR(p) ((const void __attribute__((address_space(1)))*)(p))
 #define LPTR(p) ((void __attribute__((address_space(3)))*)(p))
@@ -582,7 +586,7 @@ gemm1_prep_kernel(const uint32_t* __restrict__ q_scale, const int32_t* __restric
             return int4{e, nt, r0, nvalid | (mtile << 9)};
         };
         const int nx = G / kXcds;                  // workgroups per XCD
-        if (KB < kBalanceMinKb || G % kXcds != 0 || nx < 1 || nx > MOE_WAVE) {
+        if (KB < kBalanceMinKb || G % kXcds != 0 || nx < 1 || nx > kPlanMaxNx || total > kPlanMaxTiles) {
             // plain round-robin over the natural order
             for (int t = tid; t < total; t += 256) tiles[1 + t] = natural(t);
             if (tid == 0) tiles[0] = int4{total, 0, 0, 0};
@@ -596,39 +600,49 @@ gemm1_prep_kernel(const uint32_t* __restrict__ q_scale, const int32_t* __restric
             // whole weight slab whatever its rows).  Slot (round r, workgroup (x, j))
             // is descriptor 1 + r * G + x * nx + j; a round with fewer tiles than
             // workgroups (only the last) leaves idle slots (zero rows), which end
-            // their workgroups.  Wavefront wv plans XCDs wv and wv + 4.
-            __shared__ int rank_tile[256 / MOE_WAVE][MOE_WAVE];
+            // their workgroups.  Three phases: every tile's row count into LDS (all
+            // threads); the rounds in order, the eight XCDs at once (wavefront wv,
+            // half h plans XCD wv + 4 h, lane j of the half for workgroup j), each slot
+            // recording its tile's natural index; the descriptors of all slots (all
+            // threads).
+            __shared__ uint8_t rows_of[kPlanMaxTiles];
+            __shared__ int rank_tile[kXcds][kPlanMaxNx];
+            for (int t = tid; t < total; t += 256) rows_of[t] = (uint8_t)(natural(t).w & 511);
+            __syncthreads();
             const int R = (total + G - 1) / G;                              // rounds
-            auto cost = [&](const int4 dsc) __attribute__((always_inline)) {
-                return 700 + (300 * (dsc.w & 511)) / BM;
-            };
-            for (int x = wv; x < kXcds; x += 256 / MOE_WAVE) {
-                int acc = 0;                                       // lane j < nx: workgroup j's work so far
-                for (int r = 0; r < R; ++r) {
-                    const int c0 = r * G + x * nx;
-                    const int m = max(0, min(nx, total - c0));     // tiles of this round
-                    const int4 d = lane < m ? natural(c0 + lane) : int4{0, 0, 0, 0};
-                    const int tc = lane < m ? cost(d) : -1;
-                    // tiles by cost, descending; workgroups by work, ascending (ties: lower lane first)
-                    int trank = 0, wrank = 0;
-                    for (int k = 0; k < nx; ++k) {
-                        const int ck = __shfl(tc, k, MOE_WAVE), ak = __shfl(acc, k, MOE_WAVE);
-                        trank += (ck > tc || (ck == tc && k < lane)) ? 1 : 0;
-                        wrank += (ak < acc || (ak == acc && k < lane)) ? 1 : 0;
+            auto cost = [&](int rows) __attribute__((always_inline)) { return 700 + (300 * rows) / BM; };
+            const int half = lane >> 5, j = lane & 31, hbase = lane & 32;
+            const int x = wv + 4 * half;
+            int acc = 0;                                       // workgroup j's work so far
+            for (int r = 0; r < R; ++r) {
+                const int c0 = r * G + x * nx;
+                const int m = max(0, min(nx, total - c0));     // tiles of this round
+                const int tc = j < m ? cost(rows_of[c0 + j]) : -1;
+                // tiles by cost, descending; workgroups by work, ascending (ties: lower lane first)
+                int trank = 0, wrank = 0;
+#pragma unroll
+                for (int k = 0; k < kPlanMaxNx; ++k) {
+                    const int ck = __shfl(tc, hbase + k, MOE_WAVE), ak = __shfl(acc, hbase + k, MOE_WAVE);
+                    if (k < nx) {
+                        trank += (ck > tc || (ck == tc && k < j)) ? 1 : 0;
+                        wrank += (ak < acc || (ak == acc && k < j)) ? 1 : 0;
                     }
-                    if (lane < nx) rank_tile[wv][trank] = lane;
-                    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-                    __builtin_amdgcn_wave_barrier();
-                    const int tl = lane < nx ? rank_tile[wv][wrank] : 0;   // the lane holding this workgroup's tile
-                    const int4 mine = int4{__shfl(d.x, tl, MOE_WAVE), __shfl(d.y, tl, MOE_WAVE),
-                                           __shfl(d.z, tl, MOE_WAVE), __shfl(d.w, tl, MOE_WAVE)};
-                    if (lane < nx) {
-                        tiles[1 + r * G + x * nx + lane] = tl < m ? mine : int4{0, 0, 0, 0};
-                        acc += tl < m ? cost(mine) : 0;
-                    }
-                    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-                    __builtin_amdgcn_wave_barrier();
                 }
+                if (j < nx) rank_tile[x][trank] = j;
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                const int tl = j < nx ? rank_tile[x][wrank] : nx;   // this workgroup's tile, as a lane
+                if (j < nx) {
+                    tiles[1 + r * G + x * nx + j] = int4{tl < m ? c0 + tl : -1, 0, 0, 0};
+                    acc += tl < m ? cost(rows_of[c0 + tl]) : 0;
+                }
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+            }
+            __syncthreads();
+            for (int sl = tid; sl < R * G; sl += 256) {
+                const int t = tiles[1 + sl].x;
+                tiles[1 + sl] = t >= 0 ? natural(t) : int4{0, 0, 0, 0};
             }
             if (tid == 0) tiles[0] = int4{R * G, 0, 0, 0};
         }
