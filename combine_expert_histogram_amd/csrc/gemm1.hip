@@ -80,9 +80,9 @@ constexpr int kPrepWgPerCu = 4;   // gather workgroups of the pre-pass per CU
 // leave up to one grid's worth of idle slots); also the largest main grid
 constexpr int kMaxGrid = 1024;
 // the cost-balanced tile schedule is used for K loops of at least this many
-// steps (GEMM1's 56: -5 %); with short tiles (GEMM2's 16 steps) the drift it
-// introduces between the workgroups that share a weight slab cost more L2
-// reuse than it saved (+10 %), so those keep the plain round-robin
+// steps (GEMM1's 56: -5 % and more); with short tiles (GEMM2's 16 steps) the
+// drift it introduces between the workgroups that share a weight slab cost
+// more L2 reuse than it saved (+18 %), so those keep the plain round-robin
 constexpr int kBalanceMinKb = 32;
 // the planner's limits: 32 workgroups per XCD (a half wavefront each), and a
 // row count per tile in LDS (one byte each)
