@@ -84,10 +84,11 @@ constexpr int kMaxGrid = 1024;
 // drift it introduces between the workgroups that share a weight slab cost
 // more L2 reuse than it saved (+18 %), so those keep the plain round-robin
 constexpr int kBalanceMinKb = 32;
-// the planner's limits: 32 workgroups per XCD (a half wavefront each), and a
-// row count per tile in LDS (one byte each)
+// the planner's limits: 32 workgroups per XCD (a half wavefront each), and
+// every tile's expert in LDS (two bytes each; 24 KB keeps four gather
+// workgroups of the pre-pass on a CU)
 constexpr int kPlanMaxNx = 32;
-constexpr int kPlanMaxTiles = 16384;
+constexpr int kPlanMaxTiles = 12288;
 
 #define GPTR(p) ((const void __attribute__((address_space(1)))*)(p))
 #define LPTR(p) ((void __attribute__((address_space(3)))*)(p))
@@ -600,15 +601,24 @@ gemm1_prep_kernel(const uint32_t* __restrict__ q_scale, const int32_t* __restric
             // whole weight slab whatever its rows).  Slot (round r, workgroup (x, j))
             // is descriptor 1 + r * G + x * nx + j; a round with fewer tiles than
             // workgroups (only the last) leaves idle slots (zero rows), which end
-            // their workgroups.  Three phases: every tile's row count into LDS (all
-            // threads); the rounds in order, the eight XCDs at once (wavefront wv,
-            // half h plans XCD wv + 4 h, lane j of the half for workgroup j), each slot
-            // recording its tile's natural index; the descriptors of all slots (all
-            // threads).
-            __shared__ uint8_t rows_of[kPlanMaxTiles];
+            // their workgroups.  Every tile's expert goes to LDS first (each thread
+            // fills its experts' ranges), so a tile's descriptor is a few reads and
+            // integer operations; then the rounds, in order, the eight XCDs at once:
+            // wavefront wv, half h plans XCD wv + 4 h, lane j of the half for
+            // workgroup j.
+            __shared__ uint16_t e_of[kPlanMaxTiles];
             __shared__ int rank_tile[kXcds][kPlanMaxNx];
-            for (int t = tid; t < total; t += 256) rows_of[t] = (uint8_t)(natural(t).w & 511);
+            for (int e = tid; e < L; e += 256)
+                for (int t = tstart[e]; t < min(tstart[e + 1], total); ++t) e_of[t] = (uint16_t)e;
             __syncthreads();
+            auto desc = [&](int t) __attribute__((always_inline)) {
+                const int e = e_of[t];
+                const int mt = (eoff[e + 1] - eoff[e] + BM - 1) / BM;
+                const int local = t - tstart[e];
+                const int nt = local / mt, mtile = local - nt * mt;
+                const int r0 = eoff[e] + mtile * BM;
+                return int4{e, nt, r0, min(BM, eoff[e + 1] - r0) | (mtile << 9)};
+            };
             const int R = (total + G - 1) / G;                              // rounds
             auto cost = [&](int rows) __attribute__((always_inline)) { return 700 + (300 * rows) / BM; };
             const int half = lane >> 5, j = lane & 31, hbase = lane & 32;
@@ -617,7 +627,8 @@ gemm1_prep_kernel(const uint32_t* __restrict__ q_scale, const int32_t* __restric
             for (int r = 0; r < R; ++r) {
                 const int c0 = r * G + x * nx;
                 const int m = max(0, min(nx, total - c0));     // tiles of this round
-                const int tc = j < m ? cost(rows_of[c0 + j]) : -1;
+                const int4 d = j < m ? desc(c0 + j) : int4{0, 0, 0, 0};
+                const int tc = j < m ? cost(d.w & 511) : -1;
                 // tiles by cost, descending; workgroups by work, ascending (ties: lower lane first)
                 int trank = 0, wrank = 0;
 #pragma unroll
@@ -631,18 +642,16 @@ gemm1_prep_kernel(const uint32_t* __restrict__ q_scale, const int32_t* __restric
                 if (j < nx) rank_tile[x][trank] = j;
                 __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
                 __builtin_amdgcn_wave_barrier();
-                const int tl = j < nx ? rank_tile[x][wrank] : nx;   // this workgroup's tile, as a lane
+                const int tl = j < nx ? rank_tile[x][wrank] : 0;   // this workgroup's tile, as a lane of the half
+                const int src = hbase + tl;
+                const int4 mine = int4{__shfl(d.x, src, MOE_WAVE), __shfl(d.y, src, MOE_WAVE),
+                                       __shfl(d.z, src, MOE_WAVE), __shfl(d.w, src, MOE_WAVE)};
                 if (j < nx) {
-                    tiles[1 + r * G + x * nx + j] = int4{tl < m ? c0 + tl : -1, 0, 0, 0};
-                    acc += tl < m ? cost(rows_of[c0 + tl]) : 0;
+                    tiles[1 + r * G + x * nx + j] = tl < m ? mine : int4{0, 0, 0, 0};
+                    acc += tl < m ? cost(mine.w & 511) : 0;
                 }
                 __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
                 __builtin_amdgcn_wave_barrier();
-            }
-            __syncthreads();
-            for (int sl = tid; sl < R * G; sl += 256) {
-                const int t = tiles[1 + sl].x;
-                tiles[1 + sl] = t >= 0 ? natural(t) : int4{0, 0, 0, 0};
             }
             if (tid == 0) tiles[0] = int4{R * G, 0, 0, 0};
         }
