@@ -595,19 +595,23 @@ gemm1_prep_kernel(const uint32_t* __restrict__ q_scale, const int32_t* __restric
             // Balanced static schedule.  Round r gives XCD x the natural tiles
             // [r * G + x * nx, + nx), as the plain round-robin does, so the row tiles
             // that share a weight slab run in one round on one XCD (together in its
-            // L2).  Within the round they go to the XCD's workgroups by cost: the
-            // costliest tile to the workgroup with the least work so far.  Cost: a
-            // full tile 1000, a partial one 700 + 300 * rows / BM (a tile streams its
-            // whole weight slab whatever its rows).  Slot (round r, workgroup (x, j))
-            // is descriptor 1 + r * G + x * nx + j; a round with fewer tiles than
-            // workgroups (only the last) leaves idle slots (zero rows), which end
-            // their workgroups.  Every tile's expert goes to LDS first (each thread
-            // fills its experts' ranges), so a tile's descriptor is a few reads and
-            // integer operations; then the rounds, in order, the eight XCDs at once:
-            // wavefront wv, half h plans XCD wv + 4 h, lane j of the half for
-            // workgroup j.
+            // L2).  Within the round they go to the XCD's workgroups so that the work
+            // evens out: a partial tile (an expert's last rows) costs about 0.7 of a
+            // full one (it streams its whole weight slab whatever its rows), so the
+            // workgroups that have had the fewest partial tiles carry the most work.
+            // The XCD keeps a cyclic pointer to the next of them: a round's partial
+            // tiles go to the workgroups from the pointer on, its full tiles to the
+            // rest, and the pointer moves past the partial ones (the costliest tile
+            // to the least-loaded workgroup, as a longest-processing-time rule would
+            // do with these two costs); in a round with fewer tiles than workgroups
+            // (only the last) the idle slots (zero rows), which end their workgroups,
+            // go first, to the most-loaded ones.  Slot (round r, workgroup (x, w)) is
+            // descriptor 1 + r * G + x * nx + w.  Every tile's expert goes to LDS
+            // first (each thread fills its experts' ranges), so a tile's descriptor
+            // is a few reads and integer operations; then the rounds, in order, the
+            // eight XCDs at once: wavefront wv, half h plans XCD wv + 4 h, lane j of
+            // the half for the round's tile j.
             __shared__ uint16_t e_of[kPlanMaxTiles];
-            __shared__ int rank_tile[kXcds][kPlanMaxNx];
             for (int e = tid; e < L; e += 256)
                 for (int t = tstart[e]; t < min(tstart[e + 1], total); ++t) e_of[t] = (uint16_t)e;
             __syncthreads();
@@ -620,38 +624,26 @@ gemm1_prep_kernel(const uint32_t* __restrict__ q_scale, const int32_t* __restric
                 return int4{e, nt, r0, min(BM, eoff[e + 1] - r0) | (mtile << 9)};
             };
             const int R = (total + G - 1) / G;                              // rounds
-            auto cost = [&](int rows) __attribute__((always_inline)) { return 700 + (300 * rows) / BM; };
-            const int half = lane >> 5, j = lane & 31, hbase = lane & 32;
+            const int half = lane >> 5, j = lane & 31;
             const int x = wv + 4 * half;
-            int acc = 0;                                       // workgroup j's work so far
+            const uint64_t half_mask = half ? 0xFFFFFFFF00000000ull : 0x00000000FFFFFFFFull;
+            const uint64_t below = moe::lanemask_lt() & half_mask;         // this half's lanes below j
+            int ptr = 0;                                                    // the XCD's cyclic pointer
             for (int r = 0; r < R; ++r) {
                 const int c0 = r * G + x * nx;
-                const int m = max(0, min(nx, total - c0));     // tiles of this round
+                const int m = max(0, min(nx, total - c0));                  // tiles of this round
                 const int4 d = j < m ? desc(c0 + j) : int4{0, 0, 0, 0};
-                const int tc = j < m ? cost(d.w & 511) : -1;
-                // tiles by cost, descending; workgroups by work, ascending (ties: lower lane first)
-                int trank = 0, wrank = 0;
-#pragma unroll
-                for (int k = 0; k < kPlanMaxNx; ++k) {
-                    const int ck = __shfl(tc, hbase + k, MOE_WAVE), ak = __shfl(acc, hbase + k, MOE_WAVE);
-                    if (k < nx) {
-                        trank += (ck > tc || (ck == tc && k < j)) ? 1 : 0;
-                        wrank += (ak < acc || (ak == acc && k < j)) ? 1 : 0;
-                    }
-                }
-                if (j < nx) rank_tile[x][trank] = j;
-                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                const int tl = j < nx ? rank_tile[x][wrank] : 0;   // this workgroup's tile, as a lane of the half
-                const int src = hbase + tl;
-                const int4 mine = int4{__shfl(d.x, src, MOE_WAVE), __shfl(d.y, src, MOE_WAVE),
-                                       __shfl(d.z, src, MOE_WAVE), __shfl(d.w, src, MOE_WAVE)};
-                if (j < nx) {
-                    tiles[1 + r * G + x * nx + j] = tl < m ? mine : int4{0, 0, 0, 0};
-                    acc += tl < m ? cost(mine.w & 511) : 0;
-                }
-                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-                __builtin_amdgcn_wave_barrier();
+                const bool part = j < m && (d.w & 511) < BM;
+                const uint64_t pb = __ballot(part) & half_mask;
+                const int kp = __popcll(pb), ip = __popcll(pb & below);     // partial tiles; this one's index
+                const int idle = nx - m;
+                int w;                                                      // the workgroup of lane j's slot
+                if (j >= m) w = j - m;                                     // idle slots first
+                else if (part) w = idle + ip;
+                else w = idle + kp + (j - ip);
+                w = (ptr + w) % nx;
+                if (j < nx) tiles[1 + r * G + x * nx + w] = j < m ? d : int4{0, 0, 0, 0};
+                ptr = (ptr + kp) % nx;
             }
             if (tid == 0) tiles[0] = int4{R * G, 0, 0, 0};
         }
