@@ -37,7 +37,10 @@
 // tile's last steps and epilogue.  One workgroup barrier per K step g: before
 // it the loaders have waited (explicit vmcnt) for stage g; after it the compute
 // wavefronts read stage g while the loaders refill the stage that step g-1
-// read.  Each lane of a direct-to-LDS load lands at base + 16 * lane; the
+// read.  The compute wavefronts take barrier g inside step g-1, as soon as
+// every fragment of step g-1 is in their registers, and issue step g-1's last
+// column group of MFMAs after it, between their first reads of stage g (except
+// across a tile boundary).  Each lane of a direct-to-LDS load lands at base + 16 * lane; the
 // swizzle of the 16 B chunks inside a 128 B row (chunk c of row r sits in slot
 // c ^ (r & 7) ^ ((r >> 3) & 1)) is made by choosing which global chunk each
 // lane fetches: 16 consecutive rows read at one chunk then hit 16 distinct
@@ -96,6 +99,8 @@ constexpr int kPlanMaxTiles = 12288;
 // s_waitcnt immediate waiting until at most n vector-memory ops are outstanding
 // (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14)
 constexpr int wait_vm(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14); }
+// s_waitcnt immediate waiting until every LDS operation has returned (lgkmcnt(0))
+constexpr int kWaitLds0 = 0xF | (0x7 << 4) | (0x3 << 14);
 
 // s_waitcnt vmcnt(n) for a wave-uniform n in [LO, HI] (the count is an
 // immediate of the instruction, so each value is its own instruction)
@@ -116,12 +121,10 @@ __device__ __forceinline__ void cbarrier() {
 }
 
 // Tile configuration: BM x 256 tile, WM x WN compute wavefronts, NLW loader
-// wavefronts, NSTAGE-deep K ring; LAG places the fold of each MFMA product
-// (-1: right after its MFMA, 0: after the column group's MFMAs, 1: one column
-// group later).
-template <int BM_, int WM_, int WN_, int NLW_, int NSTAGE_, int LAG_>
+// wavefronts, NSTAGE-deep K ring.
+template <int BM_, int WM_, int WN_, int NLW_, int NSTAGE_>
 struct Cfg {
-    static constexpr int BM = BM_, WM = WM_, WN = WN_, NLW = NLW_, NSTAGE = NSTAGE_, LAG = LAG_;
+    static constexpr int BM = BM_, WM = WM_, WN = WN_, NLW = NLW_, NSTAGE = NSTAGE_;
     static constexpr int kCompute = WM * WN, kWaves = kCompute + NLW, kThreads = kWaves * MOE_WAVE;
     static constexpr int RW = BM / WM, CW = BN / WN, MI = RW / 16, NJ = CW / 16;
     static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
@@ -137,7 +140,6 @@ struct Cfg {
                   "whole 1 KB loads");
     static_assert(NLW * 64 >= BM && BM >= kMinBM && kThreads <= 1024, "scale rows, descriptors, size");
     static_assert(NSTAGE >= 2 && NSTAGE <= 4 && NSTAGE * STAGE <= 160 * 1024 && 2 * NLD < 64, "ring");
-    static_assert(LAG >= -1 && LAG <= 1, "fold placement");
 };
 
 // MX: the operands carry e8m0 scales per 32 K elements (packed four per dword:
@@ -329,50 +331,56 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
             for (int i = 0; i < MI; ++i) wr[i] = wtab[r0 + min(wm * RW + i * 16 + (lane & 15), nvalid - 1)];
         }
 
-        for (int kb = 0; kb < KB; ++kb, ++g) {
-            cbarrier();
-            if (!active) continue;
-            const uint8_t* As = ring + (g % NSTAGE) * STAGE;
-            const uint8_t* Bs = As + A_BYTES;
-            const float* Ss = reinterpret_cast<const float*>(Bs + B_BYTES);
-            if constexpr (MX) {
-                // hardware K order of the 16x16x128 fp8 operand: lane quarter q holds
-                // K [16q, 16q+16) and [64+16q, 64+16q+16), K chunks q and 4+q, which the
-                // loaders placed at logical chunks 2q and 2q+1; the scale of (row or
-                // column l & 15, K group l >> 4) comes from lane l
-                const uint32_t* Sa = reinterpret_cast<const uint32_t*>(Bs + B_BYTES);
-                const uint32_t* Sb = Sa + C::NLW * 64;
-                const int qq = lane >> 4;
-                v8i af[MI];
-                int sa[MI];
+        // The barrier of step g+1 is taken inside step g, once every fragment of
+        // step g is in registers (after the read of the last column group's B
+        // fragment): the last column group's MFMAs then run after the barrier,
+        // interleaved with the first reads of step g+1, so the MFMA pipe has work
+        // while those reads are in flight instead of idling at the start of every
+        // step.  A tile's last step keeps its barrier at the top of the next tile:
+        // the epilogue stages its outputs in that step's ring slot, which the
+        // loaders refill only after that barrier.  Inactive wavefronts take the
+        // same barriers (one per step).
+        if (!active) {
+            for (int kb = 0; kb < KB; ++kb, ++g) cbarrier();
+        } else if constexpr (MX) {
+            // hardware K order of the 16x16x128 fp8 operand: lane quarter q holds
+            // K [16q, 16q+16) and [64+16q, 64+16q+16), K chunks q and 4+q, which the
+            // loaders placed at logical chunks 2q and 2q+1; the scale of (row or
+            // column l & 15, K group l >> 4) comes from lane l
+            const int qq = lane >> 4;
+            auto read_a = [&](const uint8_t* As, int i, v8i& a, int& sa) __attribute__((always_inline)) {
+                const int row = wm * RW + i * 16 + (lane & 15);
+                const int sw_r = (row & 7) ^ ((row >> 3) & 1);
+                const u32x4 a0 = *reinterpret_cast<const u32x4*>(As + row * BK + (((2 * qq) ^ sw_r) << 4));
+                const u32x4 a1 = *reinterpret_cast<const u32x4*>(As + row * BK + (((2 * qq + 1) ^ sw_r) << 4));
+                a = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+                const uint32_t* Sa = reinterpret_cast<const uint32_t*>(As + A_BYTES + B_BYTES);
+                sa = (int)((Sa[row] >> (8 * qq)) & 0xFFu);
+            };
+            auto read_b = [&](const uint8_t* As, int j, uint32_t& sraw) __attribute__((always_inline)) {
+                const uint8_t* Bs = As + A_BYTES;
+                const uint32_t* Sb = reinterpret_cast<const uint32_t*>(Bs + B_BYTES) + C::NLW * 64;
+                const int col = wn * CW + j * 16 + (lane & 15);
+                const int sw_c = (col & 7) ^ ((col >> 3) & 1);
+                const u32x4 b0 = *reinterpret_cast<const u32x4*>(Bs + col * BK + (((2 * qq) ^ sw_c) << 4));
+                const u32x4 b1 = *reinterpret_cast<const u32x4*>(Bs + col * BK + (((2 * qq + 1) ^ sw_c) << 4));
+                sraw = Sb[col];
+                return v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+            };
+            v8i af[MI], bnext;
+            int sa[MI];
+            uint32_t sbn;
+            // column groups 0 .. NJ-2 of a step; the next group's reads are issued
+            // before this group's MFMAs (left alone, the compiler reuses one register
+            // set and waits on every read)
+            auto groups = [&](const uint8_t* As) __attribute__((always_inline)) {
 #pragma unroll
-                for (int i = 0; i < MI; ++i) {
-                    const int row = wm * RW + i * 16 + (lane & 15);
-                    const int sw_r = (row & 7) ^ ((row >> 3) & 1);
-                    const u32x4 a0 = *reinterpret_cast<const u32x4*>(As + row * BK + (((2 * qq) ^ sw_r) << 4));
-                    const u32x4 a1 = *reinterpret_cast<const u32x4*>(As + row * BK + (((2 * qq + 1) ^ sw_r) << 4));
-                    af[i] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-                    sa[i] = (int)((Sa[row] >> (8 * qq)) & 0xFFu);
-                }
-                auto read_b = [&](int j, uint32_t& sraw) __attribute__((always_inline)) {
-                    const int col = wn * CW + j * 16 + (lane & 15);
-                    const int sw_c = (col & 7) ^ ((col >> 3) & 1);
-                    const u32x4 b0 = *reinterpret_cast<const u32x4*>(Bs + col * BK + (((2 * qq) ^ sw_c) << 4));
-                    const u32x4 b1 = *reinterpret_cast<const u32x4*>(Bs + col * BK + (((2 * qq + 1) ^ sw_c) << 4));
-                    sraw = Sb[col];
-                    return v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-                };
-                uint32_t sbn;
-                v8i bnext = read_b(0, sbn);
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) {
+                for (int j = 0; j < NJ - 1; ++j) {
                     const v8i bf = bnext;
                     // the code is extracted here, after the fence below of the group
                     // before, so only this group's scale read is waited on
                     const int sb = (int)((sbn >> (8 * qq)) & 0xFFu);
-                    if (j + 1 < NJ) bnext = read_b(j + 1, sbn);
-                    // keep the next group's reads ahead of this group's MFMAs (left
-                    // alone, the compiler reuses one register set and waits on every read)
+                    bnext = read_b(As, j + 1, sbn);
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int i = 0; i < MI; ++i)
@@ -381,10 +389,43 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
                             bf, af[i], acc[i][j], 0, 0, 0, sb, 0, sa[i]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                continue;
+            };
+            cbarrier();
+            {
+                const uint8_t* As = ring + (g % NSTAGE) * STAGE;
+#pragma unroll
+                for (int i = 0; i < MI; ++i) read_a(As, i, af[i], sa[i]);
+                bnext = read_b(As, 0, sbn);
             }
-            // B fragment of column group j; group j+1's is read before group j's MFMAs
-            auto read_b = [&](int j) __attribute__((always_inline)) {
+            for (int kb = 0; kb + 1 < KB; ++kb, ++g) {
+                groups(ring + (g % NSTAGE) * STAGE);
+                const v8i bf = bnext;
+                const int sb = (int)((sbn >> (8 * qq)) & 0xFFu);
+                // every read of this step has returned: its ring slot is free
+                __builtin_amdgcn_s_waitcnt(kWaitLds0);
+                cbarrier();
+                const uint8_t* As1 = ring + ((g + 1) % NSTAGE) * STAGE;
+#pragma unroll
+                for (int i = 0; i < MI; ++i) {
+                    acc[i][NJ - 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        bf, af[i], acc[i][NJ - 1], 0, 0, 0, sb, 0, sa[i]);
+                    read_a(As1, i, af[i], sa[i]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                bnext = read_b(As1, 0, sbn);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // the tile's last step: no barrier inside it
+            groups(ring + (g % NSTAGE) * STAGE);
+            const int sb = (int)((sbn >> (8 * qq)) & 0xFFu);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+                acc[i][NJ - 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    bnext, af[i], acc[i][NJ - 1], 0, 0, 0, sb, 0, sa[i]);
+            ++g;
+        } else {
+            auto read_b = [&](const uint8_t* As, int j) __attribute__((always_inline)) {
+                const uint8_t* Bs = As + A_BYTES;
                 const int col = wn * CW + j * 16 + (lane & 15);
                 const int c0 = (lane >> 4) * 2;
                 const int sw_c = (col & 7) ^ ((col >> 3) & 1);
@@ -392,59 +433,38 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
                 const u32x4 b1 = *reinterpret_cast<const u32x4*>(Bs + col * BK + (((c0 + 1) ^ sw_c) << 4));
                 return v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
             };
-            // reads in the order of first use: column group 0, the row groups, then the
-            // scales (first used by the folds of column group 0, one group later)
-            v8i bnext = read_b(0);
-            __builtin_amdgcn_sched_barrier(0);
-            v8i af[MI];
-#pragma unroll
-            for (int i = 0; i < MI; ++i) {
+            auto read_a = [&](const uint8_t* As, int i) __attribute__((always_inline)) {
                 const int row = wm * RW + i * 16 + (lane & 15);
                 const int c0 = (lane >> 4) * 2;
                 const int sw_r = (row & 7) ^ ((row >> 3) & 1);
                 const u32x4 a0 = *reinterpret_cast<const u32x4*>(As + row * BK + ((c0 ^ sw_r) << 4));
                 const u32x4 a1 = *reinterpret_cast<const u32x4*>(As + row * BK + (((c0 + 1) ^ sw_r) << 4));
-                af[i] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            const float sw = reinterpret_cast<const float*>(Bs + B_BYTES + NSA * 256)[(wn * CW) / 128];
-            float sr[MI], f[MI];
+                return v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+            };
+            // the weights' scale of this wavefront's 128-column block and its rows'
+            // scales (first used by the folds of column group 0, one group later)
+            auto read_scales = [&](const uint8_t* As, float& sw, float* sr) __attribute__((always_inline)) {
+                const uint8_t* Bs = As + A_BYTES;
+                sw = reinterpret_cast<const float*>(Bs + B_BYTES + NSA * 256)[(wn * CW) / 128];
+                const float* Ss = reinterpret_cast<const float*>(Bs + B_BYTES);
 #pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                sr[i] = Ss[wm * RW + i * 16 + (lane & 15)];
-                if constexpr (C::LAG < 1) f[i] = sr[i] * sw;
-            }
-            __builtin_amdgcn_sched_barrier(0);
+                for (int i = 0; i < MI; ++i) sr[i] = Ss[wm * RW + i * 16 + (lane & 15)];
+            };
+            v8i bnext, af[MI];
+            float sw, sr[MI], f[MI];
             v4f pp[MI];
+            // column groups 0 .. NJ-2 of a step.  Unit (j, i): the MFMA of row group i,
+            // then the fold of row group i's product from column group j-1, whose MFMA
+            // went out MI units earlier; the fences keep that order so no unit waits on
+            // its own MFMA.  Group j+1's B fragment is read before group j's MFMAs.
+            auto groups = [&](const uint8_t* As) __attribute__((always_inline)) {
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const v8i bf = bnext;
-                if (j + 1 < NJ) bnext = read_b(j + 1);
-                if constexpr (C::LAG < 0) {
+                for (int j = 0; j < NJ - 1; ++j) {
+                    const v8i bf = bnext;
+                    bnext = read_b(As, j + 1);
 #pragma unroll
                     for (int i = 0; i < MI; ++i) {
-                        const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            bf, af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) acc[i][j][v] = fmaf(p[v], f[i], acc[i][j][v]);
-                    }
-                } else if constexpr (C::LAG == 0) {
-                    v4f pc[MI];
-#pragma unroll
-                    for (int i = 0; i < MI; ++i)
                         // transposed sub-tile: lane l holds row (l & 15), columns 4*(l >> 4) + v
-                        pc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            bf, af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-                    for (int i = 0; i < MI; ++i)
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) acc[i][j][v] = fmaf(pc[i][v], f[i], acc[i][j][v]);
-                } else {
-                    // unit (j, i): the MFMA of row group i, then the fold of row group i's
-                    // product from column group j-1, whose MFMA went out MI units earlier;
-                    // the fences keep that order so no unit waits on its own MFMA
-#pragma unroll
-                    for (int i = 0; i < MI; ++i) {
                         const v4f pc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                             bf, af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
                         if (j == 1) f[i] = sr[i] * sw;
@@ -456,13 +476,63 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
-            }
-            if constexpr (C::LAG == 1) {
+            };
+            // the last column group's unit i: its MFMA and the fold of group NJ-2's product
+            auto last_unit = [&](const v8i& bf, int i) __attribute__((always_inline)) {
+                const v4f pc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    bf, af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[i][NJ - 2][v] = fmaf(pp[i][v], f[i], acc[i][NJ - 2][v]);
+                pp[i] = pc;
+            };
+            auto last_folds = [&]() __attribute__((always_inline)) {
 #pragma unroll
                 for (int i = 0; i < MI; ++i)
 #pragma unroll
                     for (int v = 0; v < 4; ++v) acc[i][NJ - 1][v] = fmaf(pp[i][v], f[i], acc[i][NJ - 1][v]);
+            };
+            cbarrier();
+            {
+                // reads in the order of first use: column group 0, the row groups, the scales
+                const uint8_t* As = ring + (g % NSTAGE) * STAGE;
+                bnext = read_b(As, 0);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < MI; ++i) {
+                    af[i] = read_a(As, i);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                read_scales(As, sw, sr);
+                __builtin_amdgcn_sched_barrier(0);
             }
+            for (int kb = 0; kb + 1 < KB; ++kb, ++g) {
+                groups(ring + (g % NSTAGE) * STAGE);
+                const v8i bf = bnext;
+                // every read of this step has returned: its ring slot is free
+                __builtin_amdgcn_s_waitcnt(kWaitLds0);
+                cbarrier();
+                const uint8_t* As1 = ring + ((g + 1) % NSTAGE) * STAGE;
+                bnext = read_b(As1, 0);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < MI; ++i) {
+                    last_unit(bf, i);
+                    af[i] = read_a(As1, i);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                last_folds();
+                read_scales(As1, sw, sr);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // the tile's last step: no barrier inside it
+            groups(ring + (g % NSTAGE) * STAGE);
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                last_unit(bnext, i);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            last_folds();
+            ++g;
         }
         // epilogue: bf16 (RNE), valid rows only.  Each 16 x 64 piece (one row group
         // of this wavefront's columns) goes through LDS so that the global stores
@@ -699,7 +769,7 @@ int cu_count() {
 // The fold one column group later, with the MFMA / fold units fenced in
 // order, measured fastest (about 10 % over folding each product at once, where
 // the wavefront waits on its own MFMA's result).
-using TileCfg = Cfg<128, 2, 4, 4, 3, 1>;
+using TileCfg = Cfg<128, 2, 4, 4, 3>;
 static_assert(TileCfg::BM <= kMaxBM, "scale table padding covers one tile");
 
 // Workspace: the row-scale table, then the tile descriptors (16 B each; the
