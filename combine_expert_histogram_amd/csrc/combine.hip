@@ -56,10 +56,10 @@ combine_kernel(const uint16_t* __restrict__ y, int64_t y_rows, const int32_t* __
         }
     }
     moe::u32x4 o;
-    o.x = moe::f32_to_bf16_rne(acc[0]) | (moe::f32_to_bf16_rne(acc[1]) << 16);
-    o.y = moe::f32_to_bf16_rne(acc[2]) | (moe::f32_to_bf16_rne(acc[3]) << 16);
-    o.z = moe::f32_to_bf16_rne(acc[4]) | (moe::f32_to_bf16_rne(acc[5]) << 16);
-    o.w = moe::f32_to_bf16_rne(acc[6]) | (moe::f32_to_bf16_rne(acc[7]) << 16);
+    o.x = moe::pack_bf16x2(acc[0], acc[1]);
+    o.y = moe::pack_bf16x2(acc[2], acc[3]);
+    o.z = moe::pack_bf16x2(acc[4], acc[5]);
+    o.w = moe::pack_bf16x2(acc[6], acc[7]);
     __builtin_nontemporal_store(o, reinterpret_cast<moe::u32x4*>(out + g * width) + c8);
     if (threadIdx.x == 0) MOE_TRACE_PUT(moe::kTrCombine, blockIdx.x, 0, 0, tr0);
 }

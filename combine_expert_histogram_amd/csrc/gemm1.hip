@@ -553,8 +553,8 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
 #pragma unroll
                         for (int v = 0; v < 4; ++v) acc[i][j][v] *= wr[i];
                     }
-                    const uint32_t lo = moe::f32_to_bf16_rne(acc[i][j][0]) | (moe::f32_to_bf16_rne(acc[i][j][1]) << 16);
-                    const uint32_t hi = moe::f32_to_bf16_rne(acc[i][j][2]) | (moe::f32_to_bf16_rne(acc[i][j][3]) << 16);
+                    const uint32_t lo = moe::pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+                    const uint32_t hi = moe::pack_bf16x2(acc[i][j][2], acc[i][j][3]);
                     // columns j*16 + 4q .. +3 = byte 32j + 8q of the 128 B row: chunk 2j + q/2
                     *reinterpret_cast<uint2*>(stg + srow * 128 + (((2 * j + (q >> 1)) ^ (srow & 7)) << 4) + (q & 1) * 8) =
                         make_uint2(lo, hi);
