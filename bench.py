@@ -258,7 +258,7 @@ def main():
                    fp32_step=lambda: (moe.quant_dispatch(d_loc, x_d, lay, q, qs),
                                       moe.grouped_gemm1(d_loc, w.N, q, qs, lay, wq_d, ws_d, y1, g_ws)))
     s2 = stage2(torch, moe, w, d_loc, lay, y1, wts_d, alg, traffic, args)
-    ceil = ceilings(torch, moe, args.copy_calib)
+    ceil = ceilings(torch, moe, args.copy_calib, U * w.H)
 
     rec = {
         "metric": METRIC, "value": graph["us_median"], "unit": "µs", "n_gpus": 1,
@@ -283,7 +283,8 @@ def main():
         "fraction_of_measured_ceilings": {
             "gemm1_vs_mfma_loop": round(gemm_tflops / ceil["mfma_fp8_tflops"], 4),
             "dispatch_combine_vs_read_stream": round(hbm_gbs / ceil["read_stream_gbs"], 4),
-            "combine_vs_read_stream": round(kernels["combine"]["achieved"] / ceil["read_stream_gbs"], 4)},
+            "combine_vs_read_stream": round(kernels["combine"]["achieved"] / ceil["read_stream_gbs"], 4),
+            "quant_vs_rw21_stream": round(kernels["quant"]["achieved"] / ceil["rw21_stream_gbs"], 4)},
     }
 
     if not args.no_cpu_baseline:
@@ -469,6 +470,9 @@ def ceiling_lib():
                                             ctypes.c_void_p, ctypes.c_void_p]
     lib.moe_ceiling_mfma_fp8.restype = ctypes.c_int
     lib.moe_ceiling_mfma_fp8.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.moe_ceiling_rw_stream.restype = ctypes.c_int
+    lib.moe_ceiling_rw_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                          ctypes.c_void_p]
     return lib
 
 
@@ -556,12 +560,15 @@ def stage1_graph(torch, moe, d, ids_d, x_d, wq_d, ws_d, lay, q, qs, y1, g_ws, w,
             "matches_eager": bool(same)}
 
 
-def ceilings(torch, moe, copy_calib):
+def ceilings(torch, moe, copy_calib, rw_out_bytes):
     """What this GPU sustains in the same run: one pass of non-temporal 16 B
     loads over 2 GiB, each workgroup reading one contiguous chunk (the HBM read
-    rate; the hot path's HBM-bound kernels mostly read), a 1 GiB
-    device-to-device copy (bytes read + written per second; its counter reading
-    also calibrates the traffic summary) and a loop of independent fp8 MFMAs."""
+    rate; the hot path's HBM-bound kernels mostly read), a stream reading two
+    bytes per byte written (the quant's mix) at the quant's own sizes
+    (`rw_out_bytes` written), timed cold after the same read flush as stage1,
+    a 1 GiB device-to-device copy (bytes read + written per second; its counter
+    reading also calibrates the traffic summary) and a loop of independent fp8
+    MFMAs."""
     import ctypes
     lib = ceiling_lib()
     st = torch.cuda.current_stream()
@@ -585,6 +592,25 @@ def ceilings(torch, moe, copy_calib):
     torch.cuda.synchronize()
     read_us = float(np.median([e[i].elapsed_time(e[i + 1]) * 1e3 for i in range(5)]))
     del rbuf, rout
+    wbytes = (int(rw_out_bytes) + 4095) // 4096 * 4096
+    src = torch.ones(2 * wbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(wbytes, dtype=torch.uint8, device="cuda")
+    flush = ReadFlush(torch)
+    rw_grid = cus * 8
+    rw_times = []
+    for i in range(7):
+        flush(st)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        if lib.moe_ceiling_rw_stream(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), wbytes,
+                                     rw_grid, ctypes.c_void_p(st.cuda_stream)):
+            raise RuntimeError("read/write-stream launch failed")
+        e1.record(st)
+        e1.synchronize()
+        if i >= 2:
+            rw_times.append(e0.elapsed_time(e1) * 1e3)
+    rw_us = float(np.median(rw_times))
+    del src, dst, flush
     a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
     reps = 3 if copy_calib else 5
@@ -612,6 +638,9 @@ def ceilings(torch, moe, copy_calib):
     flop = grid * 8 * iters * 16 * 65536
     return {"read_stream_gbs": round(rbytes / (read_us * 1e-6) / 1e9, 1),
             "read_stream_frac_of_peak": round(rbytes / (read_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "rw21_stream_gbs": round(3 * wbytes / (rw_us * 1e-6) / 1e9, 1),
+            "rw21_stream_us": round(rw_us, 2),
+            "rw21_stream_bytes": 3 * wbytes,
             "copy_gbs": round(2 * (1 << 30) / (copy_us * 1e-6) / 1e9, 1),
             "mfma_fp8_tflops": round(flop / (mfma_us * 1e-6) / 1e12, 1),
             "mfma_fp8_frac_of_peak": round(flop / (mfma_us * 1e-6) / 1e12 / FP8_PEAK_TFLOPS, 4)}

@@ -2,6 +2,13 @@
 // library, libmoe_ceiling.so, loaded only by the benchmark):
 //  * a kernel that does nothing but fp8 MFMAs, so the benchmark can report the
 //    MFMA rate this chip sustains in the same run next to the grouped GEMM1's;
+//  * a two-to-one read/write stream: each output word is the xor of two
+//    consecutive 16 B words of the source (non-temporal loads and stores, 4
+//    pairs in flight per lane, each workgroup one contiguous chunk), so the
+//    benchmark can report what this chip sustains on a mix of two bytes read
+//    per byte written, the quant's mix (measured: ≈5.2 TB/s cold for 160 MB
+//    read + 80 MB written, against ≈7 TB/s for reads alone; ordinary stores or
+//    fewer workgroups ran slower);
 //  * a read stream: one pass of 16 B loads over a buffer, each workgroup
 //    reading one contiguous chunk (8 loads in flight per lane), folded into one
 //    word per thread, so the benchmark can report the HBM read rate this chip
@@ -76,7 +83,40 @@ __global__ void __launch_bounds__(256) read_stream_kernel(const u32x4* __restric
     out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
+__global__ void __launch_bounds__(256) rw_stream_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                        int64_t n_out16, int64_t chunk) {
+    constexpr int U = 4;
+    const int64_t beg = (int64_t)blockIdx.x * chunk;
+    const int64_t end = min(n_out16, beg + chunk);
+    int64_t i = beg + threadIdx.x;
+    for (; i + (U - 1) * 256 < end; i += U * 256) {
+        u32x4 a[U], b[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            a[u] = __builtin_nontemporal_load(src + 2 * (i + u * 256));
+            b[u] = __builtin_nontemporal_load(src + 2 * (i + u * 256) + 1);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) __builtin_nontemporal_store(a[u] ^ b[u], dst + i + u * 256);
+    }
+    for (; i < end; i += 256) __builtin_nontemporal_store(src[2 * i] ^ src[2 * i + 1], dst + i);
+}
+
 }  // namespace
+
+// Writes out_bytes (a multiple of 16) to the device buffer `dst`, each 16 B word
+// the xor of two consecutive words of `src` (2 * out_bytes), with grid
+// workgroups of 256 threads on `hip_stream`, workgroup i handling the i-th of
+// grid equal contiguous chunks.  Returns 0, or -1 for bad arguments / a launch
+// error.
+extern "C" int moe_ceiling_rw_stream(const void* src, void* dst, int64_t out_bytes, int grid, void* hip_stream) {
+    if (!src || !dst || grid <= 0 || out_bytes <= 0 || out_bytes % 16 != 0) return -1;
+    const int64_t n16 = out_bytes / 16;
+    const int64_t chunk = (n16 + grid - 1) / grid;
+    hipLaunchKernelGGL(rw_stream_kernel, dim3(grid), dim3(256), 0, reinterpret_cast<hipStream_t>(hip_stream),
+                       static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16, chunk);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
 
 // Reads `bytes` (a multiple of 16) from the device buffer `buf` once with grid
 // workgroups of 256 threads on `hip_stream`, workgroup i reading the i-th of
