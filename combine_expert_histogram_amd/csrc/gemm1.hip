@@ -56,13 +56,15 @@
 // row group 0 first, the scales last: the fold that needs them comes one
 // column group later).
 //
-// Scheduling: one persistent workgroup per CU walks a tile table (experts in
-// order; per expert, column tiles outer and row tiles inner, so the row tiles
-// that share a weight slab are adjacent) that the pre-pass derives from
-// expert_offsets.  Consecutive tile ids go to workgroups of the same XCD
-// (workgroup b runs on XCD b % 8), so the row tiles sharing a weight slab meet
-// in that XCD's L2.  A compute wavefront whose 64 rows all lie past the
-// expert's last row skips its MFMAs.
+// Scheduling: one persistent workgroup per CU walks its slots of a tile table
+// that the pre-pass derives from expert_offsets.  In the natural order (experts
+// in order; per expert, column tiles outer and row tiles inner) the row tiles
+// that share a weight slab are adjacent; each round of the table gives every
+// XCD (workgroup b runs on XCD b % 8) a run of consecutive natural tiles, so
+// the row tiles sharing a slab meet in that XCD's L2.  For K loops of at least
+// 32 steps the pre-pass also balances each round's partial tiles (an expert's
+// last rows) across the XCD's workgroups (gemm1_prep_kernel).  A compute
+// wavefront whose 64 rows all lie past the expert's last row skips its MFMAs.
 #include "common.h"
 
 #include <type_traits>
