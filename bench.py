@@ -258,8 +258,9 @@ def main():
                    fp32_step=lambda: (moe.quant_dispatch(d_loc, x_d, lay, q, qs),
                                       moe.grouped_gemm1(d_loc, w.N, q, qs, lay, wq_d, ws_d, y1, g_ws)))
     s2 = stage2(torch, moe, w, d_loc, lay, y1, wts_d, alg, traffic, args)
-    ceil = ceilings(torch, moe, args.copy_calib, U * w.H)
+    ceil = ceilings(torch, moe, args.copy_calib, (U * w.H, w.T * width * 2))
 
+    vendor = vendor_gemm(torch, w, R)
     rec = {
         "metric": METRIC, "value": graph["us_median"], "unit": "µs", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(total_ms / args.steps, 4),
@@ -280,11 +281,16 @@ def main():
         "mx": mx,
         "stage2": s2,
         "ceilings": ceil,
+        "vendor_fp8_gemm": vendor,
         "fraction_of_measured_ceilings": {
             "gemm1_vs_mfma_loop": round(gemm_tflops / ceil["mfma_fp8_tflops"], 4),
             "dispatch_combine_vs_read_stream": round(hbm_gbs / ceil["read_stream_gbs"], 4),
             "combine_vs_read_stream": round(kernels["combine"]["achieved"] / ceil["read_stream_gbs"], 4),
-            "quant_vs_rw21_stream": round(kernels["quant"]["achieved"] / ceil["rw21_stream_gbs"], 4)},
+            "quant_vs_rw21_stream": round(kernels["quant"]["achieved"] / ceil["rw21_stream_gbs"], 4),
+            "combine_vs_rw81_stream": round(kernels["combine"]["achieved"] / ceil["rw81_stream_gbs"], 4),
+            "gemm1_vs_vendor_dense": round(gemm_tflops / vendor["dense_tflops"], 4) if "dense_tflops" in vendor else None,
+            "gemm1_vs_vendor_per_expert": (round(gemm_tflops / vendor["per_expert_tflops"], 4)
+                                           if "per_expert_tflops" in vendor else None)},
     }
 
     if not args.no_cpu_baseline:
@@ -560,15 +566,66 @@ def stage1_graph(torch, moe, d, ids_d, x_d, wq_d, ws_d, lay, q, qs, y1, g_ws, w,
             "matches_eager": bool(same)}
 
 
+def vendor_gemm(torch, w, R):
+    """Context, not part of the path: the vendor library's fp8 GEMM (hipBLASLt
+    through torch._scaled_mm, per-tensor scales, bf16 out) on GEMM1's shapes, in
+    the same run: one dense GEMM of all R rows against one [N, H] weight
+    matrix, and one GEMM per local expert (R / L rows each) against its own
+    weights.  Neither has the block scales, the row gather or the fold of the
+    grouped GEMM1; the dense one also streams 1/L of its weight bytes."""
+    f8 = torch.float8_e4m3fn
+    one = torch.tensor(1.0, device="cuda")
+
+    def rand(m, k):
+        return (torch.randn(m, k, device="cuda") * 0.5).to(f8)
+
+    def med(fn, iters):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(iters):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.median(ts))
+
+    flop = 2.0 * R * w.N * w.H
+    out = {"flop": flop}
+    try:
+        a, b = rand(R, w.H), rand(w.N, w.H)
+        us = med(lambda: torch._scaled_mm(a, b.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16), 10)
+        out["dense_us"] = round(us, 1)
+        out["dense_tflops"] = round(flop / (us * 1e-6) / 1e12, 1)
+        del a, b
+        rows = [R // w.L + (1 if i < R % w.L else 0) for i in range(w.L)]
+        a_s = [rand(r, w.H) for r in rows]
+        b_s = [rand(w.N, w.H) for _ in range(w.L)]
+
+        def per_expert():
+            for a_, b_ in zip(a_s, b_s):
+                torch._scaled_mm(a_, b_.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+        us = med(per_expert, 5)
+        out["per_expert_us"] = round(us, 1)
+        out["per_expert_tflops"] = round(flop / (us * 1e-6) / 1e12, 1)
+        del a_s, b_s
+    except Exception as ex:                       # the library GEMM is optional context
+        out["error"] = str(ex)[:200]
+    return out
+
+
 def ceilings(torch, moe, copy_calib, rw_out_bytes):
     """What this GPU sustains in the same run: one pass of non-temporal 16 B
     loads over 2 GiB, each workgroup reading one contiguous chunk (the HBM read
-    rate; the hot path's HBM-bound kernels mostly read), a stream reading two
-    bytes per byte written (the quant's mix) at the quant's own sizes
-    (`rw_out_bytes` written), timed cold after the same read flush as stage1,
-    a 1 GiB device-to-device copy (bytes read + written per second; its counter
-    reading also calibrates the traffic summary) and a loop of independent fp8
-    MFMAs."""
+    rate; the hot path's HBM-bound kernels mostly read), streams reading two
+    and eight bytes per byte written (the quant's and the combine's mixes) at
+    those kernels' own sizes (`rw_out_bytes` = bytes each writes), timed cold
+    after the same read flush as stage1, a 1 GiB device-to-device copy (bytes
+    read + written per second; its counter reading also calibrates the traffic
+    summary) and a loop of independent fp8 MFMAs."""
     import ctypes
     lib = ceiling_lib()
     st = torch.cuda.current_stream()
@@ -592,25 +649,28 @@ def ceilings(torch, moe, copy_calib, rw_out_bytes):
     torch.cuda.synchronize()
     read_us = float(np.median([e[i].elapsed_time(e[i + 1]) * 1e3 for i in range(5)]))
     del rbuf, rout
-    wbytes = (int(rw_out_bytes) + 4095) // 4096 * 4096
-    src = torch.ones(2 * wbytes, dtype=torch.uint8, device="cuda")
-    dst = torch.empty(wbytes, dtype=torch.uint8, device="cuda")
     flush = ReadFlush(torch)
-    rw_grid = cus * 8
-    rw_times = []
-    for i in range(7):
-        flush(st)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(st)
-        if lib.moe_ceiling_rw_stream(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), wbytes,
-                                     rw_grid, ctypes.c_void_p(st.cuda_stream)):
-            raise RuntimeError("read/write-stream launch failed")
-        e1.record(st)
-        e1.synchronize()
-        if i >= 2:
-            rw_times.append(e0.elapsed_time(e1) * 1e3)
-    rw_us = float(np.median(rw_times))
-    del src, dst, flush
+    rw = {}
+    for ratio, out_bytes in ((2, rw_out_bytes[0]), (8, rw_out_bytes[1])):
+        wbytes = (int(out_bytes) + 4095) // 4096 * 4096
+        src = torch.ones(ratio * wbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty(wbytes, dtype=torch.uint8, device="cuda")
+        times = []
+        for i in range(7):
+            flush(st)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            if lib.moe_ceiling_rw_stream(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), wbytes,
+                                         ratio, ctypes.c_void_p(st.cuda_stream)):
+                raise RuntimeError("read/write-stream launch failed")
+            e1.record(st)
+            e1.synchronize()
+            if i >= 2:
+                times.append(e0.elapsed_time(e1) * 1e3)
+        us = float(np.median(times))
+        rw[ratio] = (us, (ratio + 1) * wbytes)
+        del src, dst
+    del flush
     a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
     reps = 3 if copy_calib else 5
@@ -638,9 +698,12 @@ def ceilings(torch, moe, copy_calib, rw_out_bytes):
     flop = grid * 8 * iters * 16 * 65536
     return {"read_stream_gbs": round(rbytes / (read_us * 1e-6) / 1e9, 1),
             "read_stream_frac_of_peak": round(rbytes / (read_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "rw21_stream_gbs": round(3 * wbytes / (rw_us * 1e-6) / 1e9, 1),
-            "rw21_stream_us": round(rw_us, 2),
-            "rw21_stream_bytes": 3 * wbytes,
+            "rw21_stream_gbs": round(rw[2][1] / (rw[2][0] * 1e-6) / 1e9, 1),
+            "rw21_stream_us": round(rw[2][0], 2),
+            "rw21_stream_bytes": rw[2][1],
+            "rw81_stream_gbs": round(rw[8][1] / (rw[8][0] * 1e-6) / 1e9, 1),
+            "rw81_stream_us": round(rw[8][0], 2),
+            "rw81_stream_bytes": rw[8][1],
             "copy_gbs": round(2 * (1 << 30) / (copy_us * 1e-6) / 1e9, 1),
             "mfma_fp8_tflops": round(flop / (mfma_us * 1e-6) / 1e12, 1),
             "mfma_fp8_frac_of_peak": round(flop / (mfma_us * 1e-6) / 1e12 / FP8_PEAK_TFLOPS, 4)}
