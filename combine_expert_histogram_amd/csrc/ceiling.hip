@@ -2,13 +2,14 @@
 // library, libmoe_ceiling.so, loaded only by the benchmark):
 //  * a kernel that does nothing but fp8 MFMAs, so the benchmark can report the
 //    MFMA rate this chip sustains in the same run next to the grouped GEMM1's;
-//  * a two-to-one read/write stream: each output word is the xor of two
-//    consecutive 16 B words of the source (non-temporal loads and stores, 4
-//    pairs in flight per lane, each workgroup one contiguous chunk), so the
-//    benchmark can report what this chip sustains on a mix of two bytes read
-//    per byte written, the quant's mix (measured: ≈5.2 TB/s cold for 160 MB
-//    read + 80 MB written, against ≈7 TB/s for reads alone; ordinary stores or
-//    fewer workgroups ran slower);
+//  * read/write streams: output word i is the xor of word i of each of two (or
+//    eight) planes of the source (non-temporal loads and stores, 8 loads in
+//    flight per lane, one pass of small workgroups), so the benchmark can
+//    report what this chip sustains on a mix of two bytes read per byte
+//    written, the quant's mix, and of eight, the combine's (in a sweep over
+//    launch shapes many one-pass workgroups ran fastest: 6.1 TB/s for 1.9 GB
+//    read + 235 MB written against 5.5 TB/s with 8 workgroups a CU each
+//    streaming a contiguous chunk; ordinary loads ran slower);
 //  * a read stream: one pass of 16 B loads over a buffer, each workgroup
 //    reading one contiguous chunk (8 loads in flight per lane), folded into one
 //    word per thread, so the benchmark can report the HBM read rate this chip
@@ -83,38 +84,45 @@ __global__ void __launch_bounds__(256) read_stream_kernel(const u32x4* __restric
     out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
+// one pass per workgroup: U output words a lane (RATIO loads each), U * 256
+// consecutive words a workgroup
+template <int RATIO, int U>
 __global__ void __launch_bounds__(256) rw_stream_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
-                                                        int64_t n_out16, int64_t chunk) {
-    constexpr int U = 4;
-    const int64_t beg = (int64_t)blockIdx.x * chunk;
-    const int64_t end = min(n_out16, beg + chunk);
-    int64_t i = beg + threadIdx.x;
-    for (; i + (U - 1) * 256 < end; i += U * 256) {
-        u32x4 a[U], b[U];
+                                                        int64_t n_out16) {
+    const int64_t i0 = (int64_t)blockIdx.x * (U * 256) + threadIdx.x;
+    u32x4 a[U][RATIO];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            a[u] = __builtin_nontemporal_load(src + 2 * (i + u * 256));
-            b[u] = __builtin_nontemporal_load(src + 2 * (i + u * 256) + 1);
-        }
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int u = 0; u < U; ++u) __builtin_nontemporal_store(a[u] ^ b[u], dst + i + u * 256);
+        for (int r = 0; r < RATIO; ++r)
+            if (i0 + u * 256 < n_out16) a[u][r] = __builtin_nontemporal_load(src + r * n_out16 + i0 + u * 256);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (i0 + u * 256 >= n_out16) continue;
+        u32x4 v = a[u][0];
+#pragma unroll
+        for (int r = 1; r < RATIO; ++r) v ^= a[u][r];
+        __builtin_nontemporal_store(v, dst + i0 + u * 256);
     }
-    for (; i < end; i += 256) __builtin_nontemporal_store(src[2 * i] ^ src[2 * i + 1], dst + i);
 }
 
 }  // namespace
 
-// Writes out_bytes (a multiple of 16) to the device buffer `dst`, each 16 B word
-// the xor of two consecutive words of `src` (2 * out_bytes), with grid
-// workgroups of 256 threads on `hip_stream`, workgroup i handling the i-th of
-// grid equal contiguous chunks.  Returns 0, or -1 for bad arguments / a launch
-// error.
-extern "C" int moe_ceiling_rw_stream(const void* src, void* dst, int64_t out_bytes, int grid, void* hip_stream) {
-    if (!src || !dst || grid <= 0 || out_bytes <= 0 || out_bytes % 16 != 0) return -1;
+// Writes out_bytes (a multiple of 16) to the device buffer `dst`, 16 B word i
+// the xor of word i of each of the `ratio` (2 or 8) consecutive out_bytes-sized
+// planes of `src` (ratio * out_bytes), on `hip_stream`: one pass of 256-thread
+// workgroups, 4 (ratio 2) or 1 (ratio 8) output words a lane.  Returns 0, or -1
+// for bad arguments / a launch error.
+extern "C" int moe_ceiling_rw_stream(const void* src, void* dst, int64_t out_bytes, int ratio, void* hip_stream) {
+    if (!src || !dst || out_bytes <= 0 || out_bytes % 16 != 0 || (ratio != 2 && ratio != 8)) return -1;
     const int64_t n16 = out_bytes / 16;
-    const int64_t chunk = (n16 + grid - 1) / grid;
-    hipLaunchKernelGGL(rw_stream_kernel, dim3(grid), dim3(256), 0, reinterpret_cast<hipStream_t>(hip_stream),
-                       static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16, chunk);
+    hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+    if (ratio == 2)
+        hipLaunchKernelGGL((rw_stream_kernel<2, 4>), dim3((unsigned)((n16 + 1023) / 1024)), dim3(256), 0, st,
+                           static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
+    else
+        hipLaunchKernelGGL((rw_stream_kernel<8, 1>), dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, st,
+                           static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

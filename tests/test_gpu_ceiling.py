@@ -37,30 +37,31 @@ def test_ceiling_library_exports_its_kernels():
 def test_ceiling_calls_reject_bad_arguments_without_launching():
     lib = _lib()
     # null buffers, sizes that are not whole 16 B words, empty grids: -1 before any launch
-    assert lib.moe_ceiling_rw_stream(None, None, 1024, 4, None) == -1
-    assert lib.moe_ceiling_rw_stream(ctypes.c_void_p(16), ctypes.c_void_p(16), 1000, 4, None) == -1
-    assert lib.moe_ceiling_rw_stream(ctypes.c_void_p(16), ctypes.c_void_p(16), 1024, 0, None) == -1
+    assert lib.moe_ceiling_rw_stream(None, None, 1024, 2, None) == -1
+    assert lib.moe_ceiling_rw_stream(ctypes.c_void_p(16), ctypes.c_void_p(16), 1000, 2, None) == -1
+    assert lib.moe_ceiling_rw_stream(ctypes.c_void_p(16), ctypes.c_void_p(16), 1024, 3, None) == -1
     assert lib.moe_ceiling_read_stream(None, 1024, 4, 0, ctypes.c_void_p(16), None) == -1
     assert lib.moe_ceiling_read_stream(ctypes.c_void_p(16), 1000, 4, 0, ctypes.c_void_p(16), None) == -1
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("out_words,grid", [(1 << 16, 64), (123457, 2048), (37, 8)])
-def test_rw_stream_writes_the_xor_of_each_source_pair(out_words, grid):
+@pytest.mark.parametrize("ratio", [2, 8])
+@pytest.mark.parametrize("out_words", [1 << 16, 123457, 37])
+def test_rw_stream_writes_the_xor_of_each_source_group(out_words, ratio):
     import torch
     from gpu_helpers import require_gpu, say
     require_gpu()
-    say(f"rw stream {out_words} words, grid {grid}")
+    say(f"rw stream {out_words} words, ratio {ratio}")
     lib = _lib()
     rng = np.random.default_rng(5)
-    src = rng.integers(0, 2**32, size=(out_words, 2, 4), dtype=np.uint32)
+    src = rng.integers(0, 2**32, size=(ratio, out_words, 4), dtype=np.uint32)
     src_d = torch.from_numpy(src.view(np.int32)).cuda()
     dst_d = torch.full((out_words, 4), -7, dtype=torch.int32, device="cuda")
     st = torch.cuda.current_stream()
     assert lib.moe_ceiling_rw_stream(ctypes.c_void_p(src_d.data_ptr()), ctypes.c_void_p(dst_d.data_ptr()),
-                                     out_words * 16, grid, ctypes.c_void_p(st.cuda_stream)) == 0
+                                     out_words * 16, ratio, ctypes.c_void_p(st.cuda_stream)) == 0
     torch.cuda.synchronize()
-    want = src[:, 0, :] ^ src[:, 1, :]
+    want = np.bitwise_xor.reduce(src, axis=0)
     assert np.array_equal(dst_d.cpu().numpy().view(np.uint32), want)
 
 
