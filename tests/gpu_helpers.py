@@ -97,7 +97,7 @@ def bf16_half_ulp(r: np.ndarray) -> np.ndarray:
 
 
 class Tol(NamedTuple):
-    """A bf16 result against an fp32 reference: the verdict and the figures."""
+    """A bf16 result against an fp32 reference: pass or fail and the figures."""
     ok: bool
     rel_l2: float
     max_excess: float     # max(|err| - half a bf16 ulp of the reference): the bound's subject
