@@ -546,7 +546,18 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
         static_assert(C::CW == 64 && C::kCompute * 2048 <= STAGE, "epilogue staging: 128 B rows, 2 KB a wavefront");
         if (active) {
             uint8_t* stg = ring + ((g - 1) % NSTAGE) * STAGE + wave * 2048;
-            const int srow = lane & 15, q = lane >> 4;
+            // the lane id through an opaque move, so that the staging offsets and
+            // row indices below are computed here and not hoisted out of the tile
+            // loop: held across the K loop they cost 16 VGPRs, and at 168 one of
+            // them was spilled, whose reload made the tile's last store wait for
+            // every store before it
+            int el;
+            asm volatile("v_mov_b32 %0, %1" : "=v"(el) : "v"(lane));
+            const int srow = el & 15, q = el >> 4;
+            // MX GEMM2: the row weights' loads (issued at the tile's start) are
+            // waited for here, before any store; the in-order count would make a
+            // wait placed after a store wait for that store as well
+            if constexpr (MX && DIRECT) __builtin_amdgcn_s_waitcnt(wait_vm(0));
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
 #pragma unroll
@@ -563,7 +574,7 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
                 }
 #pragma unroll
                 for (int p = 0; p < 2; ++p) {
-                    const int rr = p * 8 + (lane >> 3), c = lane & 7;
+                    const int rr = p * 8 + (el >> 3), c = el & 7;
                     const moe::u32x4 v = *reinterpret_cast<const moe::u32x4*>(stg + rr * 128 + ((c ^ (rr & 7)) << 4));
                     const int row = wm * RW + i * 16 + rr;
                     if (row < nvalid)
