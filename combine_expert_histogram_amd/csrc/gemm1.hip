@@ -23,8 +23,8 @@
 //
 // Why loaders: the operand stream is bounded by the L2 requests a CU can keep
 // in flight (about 70 lines) and by their latency (L2 misses to HBM take
-// several times as long as hits), so the loads are the slower side of the
-// kernel.  A wavefront whose next instruction is a load that the full queue
+// several times as long as hits), so the loads alone take about as long as
+// the MFMAs alone.  A wavefront whose next instruction is a load that the full queue
 // cannot accept stalls, and the MFMAs behind it in its instruction stream
 // stall with it; when every wavefront both loads and computes, load time and
 // MFMA time add up instead of overlapping.  The compute wavefronts here never
