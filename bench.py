@@ -27,6 +27,11 @@ quant -> grouped GEMM2 with the routing weights -> combine of the local rows)
 is timed after that and reported under "stage2", with its MX variant timed
 against it in an A/B loop of the same kind under "stage2.mx".
 
+Each timed loop starts with `warmup` untimed steps (20 by default): after the
+chip has idled, the first back-to-back calls of the GEMMs run through a clock
+transient (fast for two or three calls, then up to ≈30 % slower for a few,
+settling after ≈15), which the timed steps should not sample.
+
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--no-cpu-baseline] [--copy-calib]
 """
@@ -85,7 +90,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="ep8_2048x8_h7168")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calib", action="store_true",
