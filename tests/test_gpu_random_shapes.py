@@ -9,8 +9,8 @@ every output against the oracle to the same bar as the fixed-shape tests:
   * layout (local window) and quant: bit for bit, every slot;
   * GEMM1 with fp32 scales and with e8m0 (MX) scales: every row within the
     tolerance, rows past R untouched;
-  * GEMM2 on the oracle's quantised activations: every row within the
-    tolerance, rows past R untouched;
+  * GEMM2 on the oracle's quantised activations, with fp32 and with e8m0
+    scales: every row within the tolerance, rows past R untouched;
   * combine over the all-expert layout: every token within the tolerance.
 """
 import numpy as np
@@ -138,6 +138,21 @@ def test_random_shape_chain(seed):
     ref2 = (ostage2.grouped_gemm2(q2, s2, ref["expert_offsets"], ref["row_assign"], wts, w2, w2s)
             if R else None)
     _rows_check(y2, R, ref2, "gemm2")
+
+    # MX GEMM2 on the oracle's MX-quantised activations of the same rows
+    q2m, s2m = ostage2.act_quant_mx(g1)
+    wf2 = (rng.standard_normal((L * H, inter)) * 0.02
+           * np.exp2(rng.uniform(-3, 3, (L * H, inter // 32))).repeat(32, axis=1))
+    w2m, w2mc = omx.quantise_rows(obf16.to_f32(obf16.from_f32(wf2.astype(np.float32))))
+    w2m = w2m.reshape(L, H, inter)
+    w2ms = np.ascontiguousarray(w2mc.reshape(L, H, inter // 128).transpose(0, 2, 1))
+    y2m = torch.full((rows_cap, H), Y_POISON, dtype=torch.int16, device="cuda")
+    moe.grouped_gemm2_mx(d, inter, dev(q2m), dev(s2m.view(np.int32)), lay, dev(wts.reshape(-1)), dev(w2m),
+                         dev(w2ms.view(np.int32)), y2m.view(torch.bfloat16))
+    torch.cuda.synchronize()
+    ref2m = (ostage2.grouped_gemm2_mx(q2m, s2m, ref["expert_offsets"], ref["row_assign"], wts, w2m, w2ms)
+             if R else None)
+    _rows_check(y2m, R, ref2m, "gemm2_mx")
 
     # combine over the all-expert layout (every assignment is a row)
     da = moe.Dims(S=S, Ts=Ts, k=k, E=E, e0=0, L=E, H=H)
