@@ -289,6 +289,8 @@ def main():
         "vendor_fp8_gemm": vendor,
         "fraction_of_measured_ceilings": {
             "gemm1_vs_mfma_loop": round(gemm_tflops / ceil["mfma_fp8_tflops"], 4),
+            "gemm1_mx_vs_mfma_scaled_loop": round(mx["kernels"]["gemm1_mx"]["achieved"] / ceil["mfma_fp8_scaled_tflops"],
+                                                  4),
             "dispatch_combine_vs_read_stream": round(hbm_gbs / ceil["read_stream_gbs"], 4),
             "combine_vs_read_stream": round(kernels["combine"]["achieved"] / ceil["read_stream_gbs"], 4),
             "quant_vs_rw21_stream": round(kernels["quant"]["achieved"] / ceil["rw21_stream_gbs"], 4),
@@ -479,8 +481,9 @@ def ceiling_lib():
     lib.moe_ceiling_read_stream.restype = ctypes.c_int
     lib.moe_ceiling_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                             ctypes.c_void_p, ctypes.c_void_p]
-    lib.moe_ceiling_mfma_fp8.restype = ctypes.c_int
-    lib.moe_ceiling_mfma_fp8.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    for f in (lib.moe_ceiling_mfma_fp8, lib.moe_ceiling_mfma_fp8_scaled):
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.moe_ceiling_rw_stream.restype = ctypes.c_int
     lib.moe_ceiling_rw_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                           ctypes.c_void_p]
@@ -694,12 +697,20 @@ def ceilings(torch, moe, copy_calib, rw_out_bytes):
     if lib.moe_ceiling_mfma_fp8(grid, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(st.cuda_stream)):
         raise RuntimeError("MFMA ceiling launch failed")
     torch.cuda.synchronize()
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    for i in range(3):
-        e[i].record(st)
-        lib.moe_ceiling_mfma_fp8(grid, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(st.cuda_stream))
-    e[3].record(st); torch.cuda.synchronize()
-    mfma_us = float(np.median([e[i].elapsed_time(e[i + 1]) * 1e3 for i in range(3)]))
+    # the plain and the scaled (nonzero e8m0 operands, the MX GEMM1's form) loops alternate
+    t_mfma = {False: [], True: []}
+    for i in range(6):
+        scaled = bool(i % 2)
+        fn = lib.moe_ceiling_mfma_fp8_scaled if scaled else lib.moe_ceiling_mfma_fp8
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        if fn(grid, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(st.cuda_stream)):
+            raise RuntimeError("MFMA ceiling launch failed")
+        e1.record(st)
+        torch.cuda.synchronize()
+        t_mfma[scaled].append(e0.elapsed_time(e1) * 1e3)
+    mfma_us = float(np.median(t_mfma[False]))
+    mfma_scaled_us = float(np.median(t_mfma[True]))
     flop = grid * 8 * iters * 16 * 65536
     return {"read_stream_gbs": round(rbytes / (read_us * 1e-6) / 1e9, 1),
             "read_stream_frac_of_peak": round(rbytes / (read_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
@@ -711,7 +722,8 @@ def ceilings(torch, moe, copy_calib, rw_out_bytes):
             "rw81_stream_bytes": rw[8][1],
             "copy_gbs": round(2 * (1 << 30) / (copy_us * 1e-6) / 1e9, 1),
             "mfma_fp8_tflops": round(flop / (mfma_us * 1e-6) / 1e12, 1),
-            "mfma_fp8_frac_of_peak": round(flop / (mfma_us * 1e-6) / 1e12 / FP8_PEAK_TFLOPS, 4)}
+            "mfma_fp8_frac_of_peak": round(flop / (mfma_us * 1e-6) / 1e12 / FP8_PEAK_TFLOPS, 4),
+            "mfma_fp8_scaled_tflops": round(flop / (mfma_scaled_us * 1e-6) / 1e12, 1)}
 
 
 def cpu_baseline(w, ids, lay, q, qs, y1, R, U, gpu_stage1_us):
