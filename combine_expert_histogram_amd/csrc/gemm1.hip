@@ -350,14 +350,14 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
             // loaders placed at logical chunks 2q and 2q+1; the scale of (row or
             // column l & 15, K group l >> 4) comes from lane l
             const int qq = lane >> 4;
-            auto read_a = [&](const uint8_t* As, int i, v8i& a, int& sa) __attribute__((always_inline)) {
+            auto read_a = [&](const uint8_t* As, int i, v8i& a, uint32_t& sa) __attribute__((always_inline)) {
                 const int row = wm * RW + i * 16 + (lane & 15);
                 const int sw_r = (row & 7) ^ ((row >> 3) & 1);
                 const u32x4 a0 = *reinterpret_cast<const u32x4*>(As + row * BK + (((2 * qq) ^ sw_r) << 4));
                 const u32x4 a1 = *reinterpret_cast<const u32x4*>(As + row * BK + (((2 * qq + 1) ^ sw_r) << 4));
                 a = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
                 const uint32_t* Sa = reinterpret_cast<const uint32_t*>(As + A_BYTES + B_BYTES);
-                sa = (int)((Sa[row] >> (8 * qq)) & 0xFFu);
+                sa = Sa[row];
             };
             auto read_b = [&](const uint8_t* As, int j, uint32_t& sraw) __attribute__((always_inline)) {
                 const uint8_t* Bs = As + A_BYTES;
@@ -370,7 +370,11 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
                 return v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
             };
             v8i af[MI], bnext;
-            int sa[MI];
+            // the rows' scale words as read (sa) and this step's codes extracted
+            // from them at the step's first column group (sae): the extraction
+            // waits for the read, which the next step's reads then overlap
+            uint32_t sa[MI];
+            int sae[MI];
             uint32_t sbn;
             // column groups 0 .. NJ-2 of a step; the next group's reads are issued
             // before this group's MFMAs (left alone, the compiler reuses one register
@@ -382,13 +386,17 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
                     // the code is extracted here, after the fence below of the group
                     // before, so only this group's scale read is waited on
                     const int sb = (int)((sbn >> (8 * qq)) & 0xFFu);
+                    if (j == 0) {
+#pragma unroll
+                        for (int i = 0; i < MI; ++i) sae[i] = (int)((sa[i] >> (8 * qq)) & 0xFFu);
+                    }
                     bnext = read_b(As, j + 1, sbn);
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int i = 0; i < MI; ++i)
                         // transposed sub-tile: weights' fragment and scale first
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            bf, af[i], acc[i][j], 0, 0, 0, sb, 0, sa[i]);
+                            bf, af[i], acc[i][j], 0, 0, 0, sb, 0, sae[i]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             };
@@ -410,7 +418,7 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
 #pragma unroll
                 for (int i = 0; i < MI; ++i) {
                     acc[i][NJ - 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        bf, af[i], acc[i][NJ - 1], 0, 0, 0, sb, 0, sa[i]);
+                        bf, af[i], acc[i][NJ - 1], 0, 0, 0, sb, 0, sae[i]);
                     read_a(As1, i, af[i], sa[i]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -423,7 +431,7 @@ grouped_gemm1_kernel(const uint8_t* __restrict__ q, const uint32_t* __restrict__
 #pragma unroll
             for (int i = 0; i < MI; ++i)
                 acc[i][NJ - 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    bnext, af[i], acc[i][NJ - 1], 0, 0, 0, sb, 0, sa[i]);
+                    bnext, af[i], acc[i][NJ - 1], 0, 0, 0, sb, 0, sae[i]);
             ++g;
         } else {
             auto read_b = [&](const uint8_t* As, int j) __attribute__((always_inline)) {
