@@ -1,7 +1,7 @@
 """GPU: the calls read their counts on the device, so a whole step can be
 captured once in a graph and replayed.  Each replay (with eager work and
 synchronisations in between) must reproduce the eager step bit for bit:
-layout tables, fp8 payloads and scales, GEMM1 output and the combine."""
+layout tables, fp8 payloads and scales, the GEMM and act outputs and the combine."""
 import numpy as np
 import pytest
 import torch
