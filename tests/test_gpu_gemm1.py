@@ -151,3 +151,23 @@ def test_gemm1_permutation_weights_bit_exact():
     for le in range(6):
         for r in range(offs[le], offs[le + 1]):
             np.testing.assert_array_equal(got[r], obf16.from_f32(A[ref["row_slot"][r]][perms[le]] + np.float32(0)))
+
+
+def test_gemm1_most_local_experts():
+    """L = 1024 local experts (the most the call accepts) with a K loop of 32
+    steps (so the balanced schedule's planner runs, with ≈1000 experts of a few
+    rows each, nearly every tile partial) and one column tile.  Weights are
+    random e4m3 codes (no NaN patterns) with random block scales; every row
+    within the tolerance."""
+    require_gpu()
+    rng = np.random.default_rng(23)
+    S, Ts, k, E, L, H, n = 1, 512, 8, 1024, 1024, 4096, 128
+    T = S * Ts
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    x = obf16.from_f32((rng.standard_normal((T, H)) * np.exp2(rng.uniform(-3, 3, (T, 1)))).astype(np.float32))
+    codes = rng.integers(0, 256, (L, n, H), dtype=np.uint8)
+    wq = np.where((codes & 0x7F) == 0x7F, codes ^ 0x01, codes).astype(np.uint8)      # 0x7F / 0xFF are NaN
+    ws = np.exp2(rng.uniform(-12, -6, (L, n // 128, H // 128))).astype(np.float32)
+    d = moe.Dims(S=S, Ts=Ts, k=k, E=E, e0=0, L=L, H=H)
+    say(f"gemm1 L={L} T={T} H={H} n={n}")
+    _check(d, n, ids, x, wq, ws)
