@@ -263,7 +263,7 @@ def main():
                    fp32_step=lambda: (moe.quant_dispatch(d_loc, x_d, lay, q, qs),
                                       moe.grouped_gemm1(d_loc, w.N, q, qs, lay, wq_d, ws_d, y1, g_ws)))
     s2 = stage2(torch, moe, w, d_loc, lay, y1, wts_d, alg, traffic, args)
-    ceil = ceilings(torch, moe, args.copy_calib, (U * w.H, w.T * width * 2))
+    ceil = ceilings(torch, moe, args.copy_calib, (U * w.H, w.T * width * 2, R * (w.N // 2)))
 
     vendor = vendor_gemm(torch, w, R)
     rec = {
@@ -295,6 +295,7 @@ def main():
             "combine_vs_read_stream": round(kernels["combine"]["achieved"] / ceil["read_stream_gbs"], 4),
             "quant_vs_rw21_stream": round(kernels["quant"]["achieved"] / ceil["rw21_stream_gbs"], 4),
             "combine_vs_rw81_stream": round(kernels["combine"]["achieved"] / ceil["rw81_stream_gbs"], 4),
+            "act_vs_rw41_stream": round(s2["kernels"]["silu_mul_quant"]["achieved"] / ceil["rw41_stream_gbs"], 4),
             "gemm1_vs_vendor_dense": round(gemm_tflops / vendor["dense_tflops"], 4) if "dense_tflops" in vendor else None,
             "gemm1_vs_vendor_per_expert": (round(gemm_tflops / vendor["per_expert_tflops"], 4)
                                            if "per_expert_tflops" in vendor else None)},
@@ -628,12 +629,13 @@ def vendor_gemm(torch, w, R):
 def ceilings(torch, moe, copy_calib, rw_out_bytes):
     """What this GPU sustains in the same run: one pass of non-temporal 16 B
     loads over 2 GiB, each workgroup reading one contiguous chunk (the HBM read
-    rate; the hot path's HBM-bound kernels mostly read), streams reading two
-    and eight bytes per byte written (the quant's and the combine's mixes) at
-    those kernels' own sizes (`rw_out_bytes` = bytes each writes), timed cold
-    after the same read flush as stage1, a 1 GiB device-to-device copy (bytes
-    read + written per second; its counter reading also calibrates the traffic
-    summary) and a loop of independent fp8 MFMAs."""
+    rate; the hot path's HBM-bound kernels mostly read), streams reading two,
+    eight and four bytes per byte written (the quant's, the combine's and
+    stage2's act mixes) at those kernels' own sizes (`rw_out_bytes` = bytes each
+    writes, in that order), timed cold after the same read flush as stage1, a
+    1 GiB device-to-device copy (bytes read + written per second; its counter
+    reading also calibrates the traffic summary) and loops of independent fp8
+    MFMAs, plain and with e8m0 scales."""
     import ctypes
     lib = ceiling_lib()
     st = torch.cuda.current_stream()
@@ -659,7 +661,7 @@ def ceilings(torch, moe, copy_calib, rw_out_bytes):
     del rbuf, rout
     flush = ReadFlush(torch)
     rw = {}
-    for ratio, out_bytes in ((2, rw_out_bytes[0]), (8, rw_out_bytes[1])):
+    for ratio, out_bytes in ((2, rw_out_bytes[0]), (4, rw_out_bytes[2]), (8, rw_out_bytes[1])):
         wbytes = (int(out_bytes) + 4095) // 4096 * 4096
         src = torch.ones(ratio * wbytes, dtype=torch.uint8, device="cuda")
         dst = torch.empty(wbytes, dtype=torch.uint8, device="cuda")
@@ -717,6 +719,9 @@ def ceilings(torch, moe, copy_calib, rw_out_bytes):
             "rw21_stream_gbs": round(rw[2][1] / (rw[2][0] * 1e-6) / 1e9, 1),
             "rw21_stream_us": round(rw[2][0], 2),
             "rw21_stream_bytes": rw[2][1],
+            "rw41_stream_gbs": round(rw[4][1] / (rw[4][0] * 1e-6) / 1e9, 1),
+            "rw41_stream_us": round(rw[4][0], 2),
+            "rw41_stream_bytes": rw[4][1],
             "rw81_stream_gbs": round(rw[8][1] / (rw[8][0] * 1e-6) / 1e9, 1),
             "rw81_stream_us": round(rw[8][0], 2),
             "rw81_stream_bytes": rw[8][1],

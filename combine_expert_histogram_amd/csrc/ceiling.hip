@@ -2,8 +2,8 @@
 // library, libmoe_ceiling.so, loaded only by the benchmark):
 //  * a kernel that does nothing but fp8 MFMAs, so the benchmark can report the
 //    MFMA rate this chip sustains in the same run next to the grouped GEMM1's;
-//  * read/write streams: output word i is the xor of word i of each of two (or
-//    eight) planes of the source (non-temporal loads and stores, 8 loads in
+//  * read/write streams: output word i is the xor of word i of each of two
+//    (four, or eight) planes of the source (non-temporal loads and stores, 8 loads in
 //    flight per lane, one pass of small workgroups), so the benchmark can
 //    report what this chip sustains on a mix of two bytes read per byte
 //    written, the quant's mix, and of eight, the combine's (in a sweep over
@@ -109,16 +109,21 @@ __global__ void __launch_bounds__(256) rw_stream_kernel(const u32x4* __restrict_
 }  // namespace
 
 // Writes out_bytes (a multiple of 16) to the device buffer `dst`, 16 B word i
-// the xor of word i of each of the `ratio` (2 or 8) consecutive out_bytes-sized
-// planes of `src` (ratio * out_bytes), on `hip_stream`: one pass of 256-thread
-// workgroups, 4 (ratio 2) or 1 (ratio 8) output words a lane.  Returns 0, or -1
-// for bad arguments / a launch error.
+// the xor of word i of each of the `ratio` (2, 4 or 8) consecutive
+// out_bytes-sized planes of `src` (ratio * out_bytes), on `hip_stream`: one
+// pass of 256-thread workgroups, 4 (ratio 2), 2 (ratio 4) or 1 (ratio 8)
+// output words a lane, so 8 loads a lane are in flight.  Ratio 4 is stage2's
+// act mix (four bytes read per byte written).  Returns 0, or -1 for bad
+// arguments / a launch error.
 extern "C" int moe_ceiling_rw_stream(const void* src, void* dst, int64_t out_bytes, int ratio, void* hip_stream) {
-    if (!src || !dst || out_bytes <= 0 || out_bytes % 16 != 0 || (ratio != 2 && ratio != 8)) return -1;
+    if (!src || !dst || out_bytes <= 0 || out_bytes % 16 != 0 || (ratio != 2 && ratio != 4 && ratio != 8)) return -1;
     const int64_t n16 = out_bytes / 16;
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
     if (ratio == 2)
         hipLaunchKernelGGL((rw_stream_kernel<2, 4>), dim3((unsigned)((n16 + 1023) / 1024)), dim3(256), 0, st,
+                           static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
+    else if (ratio == 4)
+        hipLaunchKernelGGL((rw_stream_kernel<4, 2>), dim3((unsigned)((n16 + 511) / 512)), dim3(256), 0, st,
                            static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
     else
         hipLaunchKernelGGL((rw_stream_kernel<8, 1>), dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, st,

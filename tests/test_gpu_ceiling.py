@@ -1,8 +1,9 @@
 """The benchmark's measurement kernels (libmoe_ceiling.so, not part of the hot
 path's C ABI): the library exports them, and on the GPU each computes what its
 rate assumes it moves — the read stream folds every word of its buffer, the
-two-to-one stream writes every output word from its two source words — so a
-ceiling the benchmark reports is a measured pass over all of its bytes."""
+read/write streams write every output word from its two, four or eight source
+words — so a ceiling the benchmark reports is a measured pass over all of its
+bytes."""
 import ctypes
 import os
 
@@ -45,7 +46,7 @@ def test_ceiling_calls_reject_bad_arguments_without_launching():
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("ratio", [2, 8])
+@pytest.mark.parametrize("ratio", [2, 4, 8])
 @pytest.mark.parametrize("out_words", [1 << 16, 123457, 37])
 def test_rw_stream_writes_the_xor_of_each_source_group(out_words, ratio):
     import torch
