@@ -13,7 +13,10 @@
 // its codes are checked to tolerance), the block |max| over the block's 8
 // lanes by DPP, the block's codes and scale by encode_block16 (exact given
 // h), and one contiguous 16 B code store per lane.  HBM bound: per row it
-// reads 4I bytes and writes I + I/32.
+// reads 4I bytes and writes I + I/32.  The GEMM1 rows are read with ordinary
+// loads (they may still be in the last-level cache right after GEMM1; 1-2 %
+// faster than non-temporal loads there and after a cache flush) and the codes
+// written with non-temporal stores.
 //
 // MX variant (the pages' e8m0 format, "Where we stand"; packed four per dword,
 // commit "ready-first / quant-lds-store"): a group of 32 elements of h is one
@@ -51,8 +54,8 @@ silu_mul_quant_kernel(const uint16_t* __restrict__ y1, const int32_t* __restrict
         const int b = act ? blk : nblk - 1;                 // idle lanes re-read the last block
         const moe::u32x4* gp = reinterpret_cast<const moe::u32x4*>(y1 + r * 2 * I + b * 128 + sub * 16);
         const moe::u32x4* up = reinterpret_cast<const moe::u32x4*>(y1 + r * 2 * I + I + b * 128 + sub * 16);
-        const moe::u32x4 g0 = __builtin_nontemporal_load(gp), g1 = __builtin_nontemporal_load(gp + 1);
-        const moe::u32x4 u0 = __builtin_nontemporal_load(up), u1 = __builtin_nontemporal_load(up + 1);
+        const moe::u32x4 g0 = *gp, g1 = *(gp + 1);
+        const moe::u32x4 u0 = *up, u1 = *(up + 1);
         const uint32_t gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
         const uint32_t uw[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
         float h[16];
